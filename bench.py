@@ -1,0 +1,169 @@
+"""Benchmark of the ternary-weight matmul on one MI355X.
+
+Default workload: 27B-class attention-projection decode, M=1, K=N=5120,
+bf16 activations, 2-bit packed weights with one fp16 scale per 128 weights,
+bf16 output.  One step = one tern_matmul call (the whole per-token hot path
+of that projection: stream the packed weights and scales, decode, sign-select
+accumulate, scale at block boundaries, reduce, round, store).  Weight copies
+rotate through >= 2 GB of distinct device buffers so that no step finds its
+weights in the 256 MB last-level cache; inputs are resident in HBM before
+timing starts.
+
+Prints ONE JSON line (rank 0).  `value` is packed-weight GB/s for M=1 decode
+configurations and TFLOP/s for batched ones, as the metric defines them.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor figure
+METRIC = ("packed-weight GB/s & % HBM peak (M=1 GEMV); TFLOP/s & % MFMA peak (M≥256)")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--config", type=int, default=2, help="workload id (workloads.CONFIGS)")
+    ap.add_argument("--shape", type=int, default=0, help="shape index inside the workload")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--rotate-gb", type=float, default=2.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(p, seconds: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+
+    o = oracle.default()
+    sh = p.shape
+    cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, cores))
+    # bounded sample: whole output columns of the problem, all rows m
+    n_cols = sh.N if sh.M * sh.K * sh.N <= 3e8 else max(threads, int(3e8 // (sh.M * sh.K)))
+    n_cols = min(n_cols, sh.N)
+    sub = p.packed[:n_cols]
+    ssc = p.scales[:n_cols]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.matmul(p.x, p.x_dtype, sub, ssc, sh.M, n_cols, sh.K, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / reps
+    if sh.M == 1:
+        val, unit = n_cols * sh.K / 4 / per / 1e9, "GB/s"
+    else:
+        val, unit = 2.0 * sh.M * n_cols * sh.K / per / 1e12, "TFLOP/s"
+    sample = (f"{reps} full oracle passes over {n_cols} of {sh.N} output columns "
+              f"(M={sh.M}, K={sh.K}), {el:.1f} s")
+    return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the ternary matmul path is built and measured per GPU, with no collectives.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    cfg = workloads.CONFIGS[args.config]
+    p = workloads.make_problem(args.config, args.shape)
+    sh = p.shape
+    dev = torch.device("cuda:0")
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+    x = torch.from_numpy(p.x.view(np.int16)).to(dev).view(tdt[p.x_dtype])
+    w0 = torch.from_numpy(p.packed).to(dev)
+    s0 = torch.from_numpy(p.scales.view(np.int16)).to(dev).view(torch.float16)
+    wbytes = w0.numel() + s0.numel() * 2
+    copies = max(1, int(np.ceil(args.rotate_gb * 1e9 / wbytes)))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    y = torch.empty((sh.M, sh.N), dtype=tdt[p.y_dtype], device=dev)
+
+    def step(i):
+        tern.matmul_into(x, ws[i % copies], ss[i % copies], y, path=args.path)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    sec = ms_step / 1e3
+
+    packed_bytes = sh.N * sh.K / 4
+    scale_bytes = sh.N * (sh.K // 128) * 2
+    xb = 2
+    yb = {"f32": 4, "bf16": 2, "f16": 2}[p.y_dtype]
+    alg_bytes = packed_bytes + scale_bytes + sh.M * sh.K * xb + sh.M * sh.N * yb
+    flops = 2.0 * sh.M * sh.N * sh.K
+    decode = sh.M <= 16
+    if decode:
+        value, unit = packed_bytes / sec / 1e9, "GB/s"
+        achieved = alg_bytes / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        value, unit = flops / sec / 1e12, "TFLOP/s"
+        achieved = flops / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.x_dtype,
+        "data": "synthetic (seeded; no model weights or datasets)",
+        "config": {"workload": f"{cfg.name}: M={sh.M} K={sh.K} N={sh.N} ({sh.label})",
+                   "M": sh.M, "K": sh.K, "N": sh.N, "group": 128, "x_dtype": p.x_dtype,
+                   "y_dtype": p.y_dtype, "path": args.path, "weight_copies": copies,
+                   "rotated_bytes": int(copies * wbytes), "parallelism": "single GPU"},
+        "roofline": roof,
+        "packed_weight_bytes": int(packed_bytes),
+        "algorithmic_bytes": int(alg_bytes),
+        "tflops": round(flops / sec / 1e12, 4),
+        "packed_GBps_frac_of_hbm_peak": round(packed_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

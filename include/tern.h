@@ -1,0 +1,127 @@
+/*
+ * tern.h -- C ABI of libtern.so, the ternary-weight matmul for AMD MI355X (gfx950).
+ *
+ * The operation (2kiu.com/news/5082861, "putting a ternary embedding model
+ * into vLLM"):
+ *   - weights W[N,K] take values in {-1, 0, +1}; each is a 2-bit code
+ *     00 -> 0, 01 -> +1, 10 -> -1, 11 -> reserved, read as 0            (§3.1)
+ *   - four codes per byte, little-endian: weight 4j+i of a row sits in
+ *     bits 2i..2i+1 of byte j of that row; packed[N, K/4] uint8         (§2.2, §3.1)
+ *   - every `group` = 128 consecutive weights of a row along K share one
+ *     fp16 scale; scales[N, K/128]                                      (§1.1, §3.1)
+ *   - Y[M,N] = X[M,K] . (T (*) S)^T, X fp16 or bf16, fp32 accumulation  (§4.2)
+ *   - callers flatten activations to a contiguous 2-D [tokens, K]      (§4.4)
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer the caller allocated and owns.  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     frees or retains a caller buffer.
+ *   - Every tensor is dense, row-major and contiguous.  Pointers to X, W, T
+ *     and packed bytes must be 16-byte aligned (TERN_ERR_ALIGN otherwise);
+ *     scales need 2-byte and Y its element alignment.
+ *   - Calls are asynchronous on `stream` (NULL = the device's default
+ *     stream) and never synchronize the host.
+ *   - Arguments are validated before anything is launched.  A non-OK status
+ *     means nothing was launched and no output byte was written, except
+ *     TERN_ERR_HIP, which reports a failed launch.
+ *   - Sizes of zero are valid: nothing is launched (tern_matmul with K = 0
+ *     and M, N > 0 writes Y = 0, the empty sum).  A pointer may be NULL only
+ *     when the buffer it stands for has zero elements.
+ *   - The library never exits the process and never throws across the ABI.
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TERN_OK = 0,
+    TERN_ERR_NULL = 1,        /* a required pointer is NULL */
+    TERN_ERR_SHAPE = 2,       /* negative size, K % 4 != 0, or a size beyond the limits below */
+    TERN_ERR_GROUP = 3,       /* K is not a multiple of `group`, or group <= 0 */
+    TERN_ERR_DTYPE = 4,       /* x or y dtype outside the supported set */
+    TERN_ERR_ALIGN = 5,       /* a pointer lacks the alignment stated above */
+    TERN_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement (group != 128, forced path that cannot run) */
+    TERN_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} tern_status;
+
+typedef enum { TERN_F16 = 0, TERN_BF16 = 1, TERN_F32 = 2 } tern_dtype;
+
+/* Which kernel family computes tern_matmul_path's result. */
+typedef enum {
+    TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does) */
+    TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
+    TERN_PATH_MFMA = 2  /* LDS-staged activations + in-register weight decode + MFMA; any M */
+} tern_path;
+
+#define TERN_GROUP 128
+#define TERN_GEMV_MAX_M 4
+/* Size limits: M, N <= 2^31 - 1 and K <= 2^30; M*N, M*K and N*K <= 2^62. */
+
+/* Human-readable name of a status code (a static string; never NULL). */
+const char *tern_status_string(tern_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int tern_version(void);
+
+/*
+ * tern_pack -- T[N,K] int8 -> packed[N,K/4] uint8.
+ * Source: 2kiu.com/news/5082861 §3.1 (code map, four codes per byte, first
+ * weight in the lowest two bits).  T holds -1, 0 or +1; any other value is
+ * written as the reserved code 11, which every reader decodes as 0.
+ * Requires K % 4 == 0 (TERN_ERR_SHAPE).  T and packed: 16-byte aligned.
+ */
+tern_status tern_pack(const int8_t *T, uint8_t *packed, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * tern_unpack -- packed[N,K/4] uint8 -> T[N,K] int8 in {-1, 0, +1}.
+ * Source: 2kiu.com/news/5082861 §3.1 (the unpack function that recovers the
+ * integer matrix from the packed bytes).  Code 11 is written as 0.
+ * Requires K % 4 == 0.  Both pointers 16-byte aligned.
+ */
+tern_status tern_unpack(const uint8_t *packed, int8_t *T, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * tern_matmul -- Y[M,N] = X[M,K] . (T (*) S)^T with fp32 accumulation.
+ * Source: 2kiu.com/news/5082861 §4.2 (the kernel contract x[M,K], w[N,K/4],
+ * scale[N,K/128], out[M,N]) with §3.1 for the weight encoding.
+ *   X        [M,K]      x_dtype TERN_F16 or TERN_BF16
+ *   packed_W [N,K/4]    uint8, the encoding of tern_pack
+ *   scales   [N,K/128]  fp16 bit patterns (little-endian), one per 128
+ *                       consecutive weights of a row
+ *   Y        [M,N]      y_dtype TERN_F32, TERN_BF16 or TERN_F16; overwritten
+ *                       (never accumulated into); fp32 results are rounded
+ *                       to nearest-even into bf16/fp16, overflow gives inf
+ *   group    must be 128 (TERN_ERR_UNSUPPORTED otherwise) and divide K
+ * Result accuracy: |Y - exact| <= 2e-3 * sum_k |X[m,k] * S[n,k/128]| + one
+ * ulp of y_dtype, for finite inputs.  The batched (MFMA) path with fp16 X
+ * forms 2*S in fp16, so it needs |S| < 32768 there.
+ */
+tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
+                        const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,
+                        int64_t K, int32_t group, hipStream_t stream);
+
+/*
+ * tern_matmul_path -- tern_matmul with an explicit kernel choice.  Same
+ * arguments, layouts and result contract as tern_matmul; `path` picks the
+ * kernel family (for tests that compare the two, and for benchmarks).
+ * TERN_PATH_GEMV with M > TERN_GEMV_MAX_M, or with an activation block too
+ * large for on-chip staging, returns TERN_ERR_UNSUPPORTED.
+ */
+tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
+                             const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M,
+                             int64_t N, int64_t K, int32_t group, tern_path path,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

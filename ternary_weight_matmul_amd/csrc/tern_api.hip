@@ -1,0 +1,122 @@
+// tern_api.hip -- the C ABI declared in include/tern.h: argument validation
+// and kernel dispatch.  Validation never touches the GPU, so a rejected call
+// launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/tern.h"
+#include "tern_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxK = int64_t(1) << 30;
+constexpr int64_t kMaxProduct = int64_t(1) << 62;
+constexpr size_t kGemvLdsLimit = 96 * 1024;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool product_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxProduct / a; }
+
+tern_status check_pack_args(const void *T, const void *P, int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxK || K % 4 != 0) return TERN_ERR_SHAPE;
+    if (!product_ok(N, K)) return TERN_ERR_SHAPE;
+    if (N == 0 || K == 0) return TERN_OK;
+    if (T == nullptr || P == nullptr) return TERN_ERR_NULL;
+    if (!aligned(T, 16) || !aligned(P, 16)) return TERN_ERR_ALIGN;
+    return TERN_OK;
+}
+
+size_t dtype_size(tern_dtype d) { return d == TERN_F32 ? 4 : 2; }
+
+tern_status check_matmul_args(const void *X, tern_dtype x_dtype, const uint8_t *W, const uint16_t *S,
+                              void *Y, tern_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+                              int32_t group) {
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxK) return TERN_ERR_SHAPE;
+    if (!product_ok(M, N) || !product_ok(M, K) || !product_ok(N, K)) return TERN_ERR_SHAPE;
+    if (K % 4 != 0) return TERN_ERR_SHAPE;
+    if (group <= 0 || K % group != 0) return TERN_ERR_GROUP;
+    if (x_dtype != TERN_F16 && x_dtype != TERN_BF16) return TERN_ERR_DTYPE;
+    if (y_dtype != TERN_F16 && y_dtype != TERN_BF16 && y_dtype != TERN_F32) return TERN_ERR_DTYPE;
+    if (group != TERN_GROUP) return TERN_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return TERN_OK;
+    if (Y == nullptr) return TERN_ERR_NULL;
+    if (!aligned(Y, dtype_size(y_dtype))) return TERN_ERR_ALIGN;
+    if (K == 0) return TERN_OK;
+    if (X == nullptr || W == nullptr || S == nullptr) return TERN_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(S, 2)) return TERN_ERR_ALIGN;
+    return TERN_OK;
+}
+
+tern_status from_hip(hipError_t e) { return e == hipSuccess ? TERN_OK : TERN_ERR_HIP; }
+
+bool gemv_fits(int64_t M, int64_t K) {
+    return M >= 1 && M <= TERN_GEMV_MAX_M && tern::gemv_lds_bytes(M, K) <= kGemvLdsLimit;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tern_status_string(tern_status status) {
+    switch (status) {
+    case TERN_OK: return "TERN_OK";
+    case TERN_ERR_NULL: return "TERN_ERR_NULL: a required pointer is NULL";
+    case TERN_ERR_SHAPE: return "TERN_ERR_SHAPE: invalid size (negative, K % 4 != 0, or beyond limits)";
+    case TERN_ERR_GROUP: return "TERN_ERR_GROUP: K is not a multiple of group, or group <= 0";
+    case TERN_ERR_DTYPE: return "TERN_ERR_DTYPE: unsupported x or y dtype";
+    case TERN_ERR_ALIGN: return "TERN_ERR_ALIGN: pointer misaligned";
+    case TERN_ERR_UNSUPPORTED: return "TERN_ERR_UNSUPPORTED: request not implemented by this build";
+    case TERN_ERR_HIP: return "TERN_ERR_HIP: HIP launch error";
+    }
+    return "TERN_ERR_UNKNOWN: not a tern_status value";
+}
+
+int tern_version(void) { return 100; }
+
+tern_status tern_pack(const int8_t *T, uint8_t *packed, int64_t N, int64_t K, hipStream_t stream) {
+    const tern_status st = check_pack_args(T, packed, N, K);
+    if (st != TERN_OK || N == 0 || K == 0) return st;
+    return from_hip(tern::launch_pack(T, packed, N * (K / 4), stream));
+}
+
+tern_status tern_unpack(const uint8_t *packed, int8_t *T, int64_t N, int64_t K, hipStream_t stream) {
+    const tern_status st = check_pack_args(T, packed, N, K);
+    if (st != TERN_OK || N == 0 || K == 0) return st;
+    return from_hip(tern::launch_unpack(packed, T, N * (K / 4), stream));
+}
+
+tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
+                             const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M,
+                             int64_t N, int64_t K, int32_t group, tern_path path,
+                             hipStream_t stream) {
+    const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group);
+    if (st != TERN_OK) return st;
+    if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA)
+        return TERN_ERR_UNSUPPORTED;
+    if (path == TERN_PATH_GEMV && M > 0 && K > 0 && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return TERN_OK;
+    if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
+
+    tern::GemmArgs a;
+    a.X = X;
+    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
+    a.W = packed_W;
+    a.S = scales;
+    a.Y = Y;
+    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.stream = stream;
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && gemv_fits(M, K));
+    return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
+}
+
+tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed_W, const uint16_t *scales,
+                        void *Y, tern_dtype y_dtype, int64_t M, int64_t N, int64_t K, int32_t group,
+                        hipStream_t stream) {
+    return tern_matmul_path(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group, TERN_PATH_AUTO,
+                            stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// tern_device.h -- device-side helpers shared by the HIP kernels of libtern.
+//
+// Weight decode (2kiu.com/news/5082861 §3.1): a 32-bit word read from a
+// packed row holds 16 consecutive weights, weight i in bits 2i..2i+1, codes
+// 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0.
+//
+// The kernels never build the integer weight.  They turn the code word into
+// pairs of 16-bit floats whose value is 2t (t in {-1,0,+1}):
+//   1. v = w ^ ((w >> 1) & 0x5555...): each 2-bit field becomes
+//      [sign = bit1, nonzero = bit0 ^ bit1]; code 11 turns into [1, 0].
+//   2. pair i (0..7) = (v << (14 - 2i)) & 0xC000C000 places the field of
+//      weight i at bits 15..14 and the field of weight i+8 at bits 31..30.
+//      A 16-bit value whose only set bits are 15 (sign) and 14 is +-2.0 in
+//      both fp16 and bf16, and +-0 when bit 14 is clear.
+// A packed dot (v_dot2_f32_f16 / _bf16) of such a pair with the activation
+// pair {x[i], x[i+8]} then adds +2x, subtracts 2x or skips, in fp32: the
+// pages' add / subtract / skip, two weights per instruction.  The factor two
+// is removed with the scale (exact: a power of two).
+//
+// Activations are stored "pair-interleaved" so the pair {x[16c+i], x[16c+i+8]}
+// is one 32-bit word: within each block of 16 elements, position 2i holds
+// element i and position 2i+1 holds element i+8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// Field transform: [bit1, bit0] -> [sign, nonzero] for all 16 fields.
+__device__ __forceinline__ uint32_t sign_nz_fields(uint32_t w) {
+    return w ^ ((w >> 1) & 0x55555555u);
+}
+
+// +-2 / 0 pair for weights (i, i+8) of a transformed word.
+template <int I>
+__device__ __forceinline__ uint32_t weight_pair(uint32_t v) {
+    static_assert(I >= 0 && I < 8, "pair index");
+    return (v << (14 - 2 * I)) & 0xC000C000u;
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi with fp16 or bf16 operands, fp32 accumulate.
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                               __builtin_bit_cast(bf162_t, b), acc, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                      __builtin_bit_cast(half2_t, b), acc, false);
+    }
+}
+
+// Pair {lo16(a), lo16(b)} and {hi16(a), hi16(b)}.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// 16 consecutive activations (two 16-byte vectors lo = x[0..7], hi = x[8..15])
+// -> 8 pair-interleaved words {x[i], x[i+8]}, i = 0..7.
+__device__ __forceinline__ void interleave16(const uint4 &lo, const uint4 &hi, uint32_t out[8]) {
+    out[0] = pair_lo(lo.x, hi.x);
+    out[1] = pair_hi(lo.x, hi.x);
+    out[2] = pair_lo(lo.y, hi.y);
+    out[3] = pair_hi(lo.y, hi.y);
+    out[4] = pair_lo(lo.z, hi.z);
+    out[5] = pair_hi(lo.z, hi.z);
+    out[6] = pair_lo(lo.w, hi.w);
+    out[7] = pair_hi(lo.w, hi.w);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// fp32 -> output element, round to nearest even (overflow -> inf).
+template <int YT>
+__device__ __forceinline__ void store_out(void *Y, int64_t idx, float v) {
+    if constexpr (YT == 2) {
+        static_cast<float *>(Y)[idx] = v;
+    } else if constexpr (YT == 1) {
+        static_cast<__bf16 *>(Y)[idx] = static_cast<__bf16>(v);
+    } else {
+        static_cast<_Float16 *>(Y)[idx] = static_cast<_Float16>(v);
+    }
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false));
+    return x;
+}
+
+}  // namespace tern

@@ -1,0 +1,37 @@
+// tern_kernels.h -- host-side launchers of the HIP kernels behind tern.h.
+// Every launcher assumes its arguments were validated by tern_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tern {
+
+struct GemmArgs {
+    const void *X;       // [M,K] fp16/bf16
+    int x_dtype;         // 0 = fp16, 1 = bf16
+    const uint8_t *W;    // [N,K/4]
+    const uint16_t *S;   // [N,K/128] fp16 bits
+    void *Y;             // [M,N]
+    int y_dtype;         // 0 = fp16, 1 = bf16, 2 = fp32
+    int64_t M, N, K;
+    hipStream_t stream;
+};
+
+// Decode-path GEMV, 1 <= M <= 4.
+hipError_t launch_gemv(const GemmArgs &a);
+// LDS bytes the GEMV needs for this M, K (it stages X[M,K] on chip).
+size_t gemv_lds_bytes(int64_t M, int64_t K);
+
+// Batched path: MFMA GEMM, any M >= 1.
+hipError_t launch_gemm(const GemmArgs &a);
+
+// Y = 0 (K == 0).
+hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
+
+// Pack / unpack over n_bytes packed bytes (= N*K/4).
+hipError_t launch_pack(const int8_t *T, uint8_t *P, int64_t n_bytes, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t *P, int8_t *T, int64_t n_bytes, hipStream_t stream);
+
+}  // namespace tern

@@ -1,0 +1,95 @@
+"""Torch-tensor entry points over the C ABI (argument marshalling only).
+
+Each function checks what only the binding can check (tensor device, dtype,
+contiguity), passes raw device pointers, sizes and the current HIP stream to
+the library, and raises TernError on a non-OK status.  The library itself
+validates shapes, group, alignment and dtypes before launching anything.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._lib import DTYPE_CODE, PATH_AUTO, PATH_GEMV, PATH_MFMA, TernError, lib
+
+_TORCH_CODE = {torch.float16: DTYPE_CODE["f16"], torch.bfloat16: DTYPE_CODE["bf16"],
+               torch.float32: DTYPE_CODE["f32"]}
+_PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int = 2) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (reshape to 2-D and call .contiguous())")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TernError(status, where)
+
+
+def pack(T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 [N,K] (values -1/0/+1) -> uint8 [N,K/4], 2 bits per weight."""
+    _need(T, "T", torch.int8)
+    N, K = T.shape
+    if out is None:
+        out = torch.empty((N, K // 4), dtype=torch.uint8, device=T.device)
+    _need(out, "out", torch.uint8)
+    if tuple(out.shape) != (N, K // 4):
+        raise ValueError("out must be [N, K/4]")
+    _check(lib.tern_pack(T.data_ptr(), out.data_ptr(), N, K, _stream(T)), "tern_pack")
+    return out
+
+
+def unpack(packed: torch.Tensor, K: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """uint8 [N,K/4] -> int8 [N,K] in {-1,0,+1}."""
+    _need(packed, "packed", torch.uint8)
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {K // 4}")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _need(out, "out", torch.int8)
+    _check(lib.tern_unpack(packed.data_ptr(), out.data_ptr(), N, K, _stream(packed)), "tern_unpack")
+    return out
+
+
+def matmul_into(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: torch.Tensor,
+                group: int = 128, path: str = "auto") -> torch.Tensor:
+    """out[M,N] = x[M,K] . (T*S)^T; x fp16/bf16, scales fp16 [N,K/group]."""
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    _need(x, "x", x.dtype)
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.float16)
+    if out.dtype not in _TORCH_CODE:
+        raise TypeError("out must be float32, bfloat16 or float16")
+    _need(out, "out", out.dtype)
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K or tuple(scales.shape) != (N, K // group if group > 0 else 0) \
+            or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, packed {tuple(packed.shape)}, "
+                         f"scales {tuple(scales.shape)}, out {tuple(out.shape)}")
+    st = lib.tern_matmul_path(x.data_ptr(), _TORCH_CODE[x.dtype], packed.data_ptr(), scales.data_ptr(),
+                              out.data_ptr(), _TORCH_CODE[out.dtype], M, N, K, group, _PATHS[path],
+                              _stream(x))
+    _check(st, "tern_matmul")
+    return out
+
+
+def matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+           out_dtype: torch.dtype = torch.bfloat16, group: int = 128, path: str = "auto") -> torch.Tensor:
+    """Y[M,N] = x[M,K] . (T*S)^T with fp32 accumulation; returns a new tensor."""
+    out = torch.empty((x.shape[0], packed.shape[0]), dtype=out_dtype, device=x.device)
+    return matmul_into(x, packed, scales, out, group, path)

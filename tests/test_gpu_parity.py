@@ -1,0 +1,272 @@
+"""HIP path vs the CPU oracle, on the GPU.
+
+Pack/unpack must be bit-exact.  Matmul outputs must satisfy
+|Y_gpu - Y_oracle| <= 2e-3 * sum_k |x[m,k] * s[n,k/128]| + one ulp of the
+output type at Y_oracle, elementwise; where the arithmetic is exact
+(integer activations, power-of-two scales) the output must equal the
+oracle's value rounded to the output type, bit for bit.  Every workload is
+seeded and synthetic (see the workloads package).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from gpu_util import (TORCH_DT, bits_to_device, check, device, out_bits, problem_to_device,  # noqa: E402
+                      run, sample_indices)
+
+tern = pytest.importorskip("ternary_weight_matmul_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+O = oracle.default
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 12), (7, 36), (64, 1024), (5, 5120), (257, 1028)])
+def test_pack_bit_exact(N, K):
+    T = workloads.draw_ternary(N * 131 + K, N, K)
+    T[0, 0] = 5 if K > 0 else 0           # an invalid value -> reserved code 11
+    got = tern.pack(torch.from_numpy(T).to(device())).cpu().numpy()
+    want = O().pack(T)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+
+
+@pytest.mark.parametrize("N,K", [(1, 1024), (3, 12), (9, 132), (128, 5120), (2, 4)])
+def test_unpack_bit_exact(N, K):
+    rng = np.random.default_rng(N + K)
+    P = rng.integers(0, 256, (N, K // 4), dtype=np.uint8)
+    if P.size >= 256:
+        P.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)   # every byte value
+    got = tern.unpack(torch.from_numpy(P).to(device()), K).cpu().numpy()
+    assert np.array_equal(got, O().unpack(P, N, K))
+
+
+def test_device_copy_and_roundtrip():
+    # the packed bytes on the device equal the host bytes; pack(unpack(P)) is P with 11 -> 00
+    rng = np.random.default_rng(5)
+    P = rng.integers(0, 256, (33, 80), dtype=np.uint8)
+    dP = torch.from_numpy(P).to(device())
+    assert np.array_equal(dP.cpu().numpy(), P)
+    back = tern.pack(tern.unpack(dP, 320)).cpu().numpy()
+    assert np.array_equal(back, O().pack(O().unpack(P, 33, 320)))
+
+
+# ---------------------------------------------------------------------------
+# matmul on the configured workloads
+# ---------------------------------------------------------------------------
+
+def _full(p, path):
+    sh = p.shape
+    y = out_bits(run(p, path), p.y_dtype)
+    Y, B = O().matmul(p.x, p.x_dtype, p.packed, p.scales, sh.M, sh.N, sh.K, threads=8)
+    return check(y, p.y_dtype, Y, B, f"{sh} {path}")
+
+
+def _sampled(p, path, count=3000, seed=0):
+    sh = p.shape
+    y = out_bits(run(p, path), p.y_dtype)
+    ms, ns = sample_indices(sh.M, sh.N, count, seed)
+    Y, B = O().matmul_at(p.x, p.x_dtype, p.packed, p.scales, sh.M, sh.N, sh.K, ms, ns)
+    return check(y[ms, ns], p.y_dtype, Y, B, f"{sh} {path}")
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "mfma"])
+def test_tiny_config(path):
+    _full(workloads.make_problem(1), path)
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "mfma"])
+def test_attention_decode_config(path):
+    _full(workloads.make_problem(2), path)
+
+
+@pytest.mark.parametrize("shape_id", range(6))
+def test_ffn_decode_config(shape_id):
+    p = workloads.make_problem(3, shape_id)
+    if p.shape.M == 1:
+        _full(p, "auto")
+    else:
+        _sampled(p, "auto", 2000, shape_id)
+
+
+@pytest.mark.parametrize("shape_id", range(4))
+def test_prefill_config(shape_id):
+    _sampled(workloads.make_problem(4, shape_id), "auto", 3000, shape_id)
+
+
+@pytest.mark.parametrize("shape_id", range(3))
+def test_embedding_config(shape_id):
+    _sampled(workloads.make_problem(5, shape_id), "auto", 3000, shape_id)
+
+
+@pytest.mark.parametrize("shape_id", [0, 3, 4, 6, 333])
+def test_sweep_matrices(shape_id):
+    _full(workloads.make_problem(6, shape_id), "auto")
+
+
+# ---------------------------------------------------------------------------
+# shapes off the tile grid, dtypes, paths
+# ---------------------------------------------------------------------------
+
+RAGGED = [(1, 128, 1), (1, 640, 33), (2, 1152, 50), (3, 384, 17), (4, 3200, 29), (1, 17408, 5),
+          (5, 256, 3), (17, 640, 100), (130, 384, 257), (129, 1152, 300), (64, 128, 512)]
+
+
+@pytest.mark.parametrize("M,K,N", RAGGED)
+@pytest.mark.parametrize("xd,yd", [("f16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
+def test_ragged_shapes(M, K, N, xd, yd):
+    p = workloads.make_custom(M * 7 + K + N, M, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.02)
+    paths = ["auto", "mfma"] + (["gemv"] if M <= tern.GEMV_MAX_M else [])
+    for path in paths:
+        _full(p, path)
+
+
+def test_outliers_and_wide_scales():
+    # activations with x20 outliers, scales spread over two decades
+    p = workloads.make_custom(77, 8, 1024, 96, x_dtype="f16", y_dtype="f32", scale_lo=1e-3, scale_hi=4.0)
+    X = p.x.view(np.float16).astype(np.float64)
+    X[:, ::37] *= 20
+    p.x = X.astype(np.float16).view(np.uint16)
+    for path in ("mfma",):
+        _full(p, path)
+    q = workloads.make_custom(78, 2, 1024, 96, x_dtype="bf16", y_dtype="bf16", scale_lo=1e-3, scale_hi=4.0)
+    for path in ("gemv", "mfma"):
+        _full(q, path)
+
+
+# ---------------------------------------------------------------------------
+# exact arithmetic: bit-exact against the oracle rounded to the output type
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16)])
+@pytest.mark.parametrize("xd", ["f16", "bf16"])
+@pytest.mark.parametrize("yd", ["f32", "bf16", "f16"])
+def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
+    rng = np.random.default_rng(M * 1000 + K + N)
+    xi = rng.integers(-8, 9, (M, K)).astype(np.float64)
+    xbits = (xi.astype(np.float16).view(np.uint16) if xd == "f16"
+             else workloads.to_bf16_bits(xi))
+    T = workloads.draw_ternary(K + N, N, K)
+    P = O().pack(T)
+    sbits = (2.0 ** rng.integers(-4, 1, (N, K // 128))).astype(np.float16).view(np.uint16)
+    Y, _ = O().matmul(xbits, xd, P, sbits, M, N, K)
+    want = O().round(Y, yd)
+    x = bits_to_device(xbits, xd)
+    w = torch.from_numpy(P).to(device())
+    s = bits_to_device(sbits, "f16")
+    for path in ["mfma"] + (["gemv"] if M <= tern.GEMV_MAX_M else []):
+        y = tern.matmul(x, w, s, out_dtype=TORCH_DT[yd], path=path)
+        got = O().decode(out_bits(y, yd), yd)
+        assert np.array_equal(got, want), (path, np.argwhere(got != want)[:5])
+
+
+# ---------------------------------------------------------------------------
+# invariants of the method, exact on the GPU
+# ---------------------------------------------------------------------------
+
+def _swap(P):
+    out = P.copy()
+    for s in (0, 2, 4, 6):
+        f = (P >> s) & 3
+        new = np.where(f == 1, 2, np.where(f == 2, 1, f)).astype(np.uint8)
+        out = (out & ~np.uint8(3 << s)) | (new << s)
+    return out
+
+
+def _reserved_to_zero(P):
+    out = P.copy()
+    for s in (0, 2, 4, 6):
+        out = np.where(((P >> s) & 3) == 3, out & ~np.uint8(3 << s), out)
+    return out
+
+
+@pytest.mark.parametrize("M,path", [(1, "gemv"), (4, "gemv"), (1, "mfma"), (96, "mfma")])
+def test_invariants_exact(M, path):
+    p = workloads.make_custom(300 + M, M, 2048, 200, x_dtype="bf16", y_dtype="f32",
+                              probs=(0.3, 0.3, 0.3, 0.1))
+    x, w, s = problem_to_device(p)
+
+    def y_of(xx, ww, ss):
+        return tern.matmul(xx, ww, ss, out_dtype=torch.float32, path=path).cpu().numpy()
+
+    y = y_of(x, w, s)
+    assert np.array_equal(y, y_of(x, w, s)), "not deterministic"
+    zero = torch.zeros_like(w)
+    assert not np.any(y_of(x, zero, s)), "all-zero codes must give exactly 0"
+    ones = torch.full_like(w, 0xFF)
+    assert not np.any(y_of(x, ones, s)), "all-reserved codes must give exactly 0"
+    ys = y_of(x, torch.from_numpy(_swap(p.packed)).to(device()), s)
+    assert np.array_equal(ys, -y), "swapping 01 and 10 must negate Y exactly"
+    yr = y_of(x, torch.from_numpy(_reserved_to_zero(p.packed)).to(device()), s)
+    assert np.array_equal(yr, y), "code 11 must act as 00"
+    y2 = y_of(x * 2, w, s)
+    assert np.array_equal(y2, 2 * y), "Y(2X) must be 2Y"
+
+
+def test_paths_agree_within_tolerance():
+    for M in (1, 2, 4):
+        p = workloads.make_custom(500 + M, M, 5120, 512, x_dtype="bf16", y_dtype="f32")
+        a = _full(p, "gemv")
+        b = _full(p, "mfma")
+        assert a <= 1 and b <= 1
+
+
+# ---------------------------------------------------------------------------
+# edge cases of the boundary
+# ---------------------------------------------------------------------------
+
+def test_k_zero_writes_zeros():
+    x = torch.empty((3, 0), dtype=torch.float16, device=device())
+    w = torch.empty((5, 0), dtype=torch.uint8, device=device())
+    s = torch.empty((5, 0), dtype=torch.float16, device=device())
+    y = torch.full((3, 5), 7.0, dtype=torch.float32, device=device())
+    tern.matmul_into(x, w, s, y)
+    assert not torch.any(y).item()
+
+
+def test_empty_m_and_n():
+    x = torch.empty((0, 256), dtype=torch.float16, device=device())
+    w = torch.zeros((4, 64), dtype=torch.uint8, device=device())
+    s = torch.ones((4, 2), dtype=torch.float16, device=device())
+    assert tern.matmul(x, w, s).shape == (0, 4)
+    x1 = torch.ones((2, 256), dtype=torch.float16, device=device())
+    w0 = torch.zeros((0, 64), dtype=torch.uint8, device=device())
+    s0 = torch.zeros((0, 2), dtype=torch.float16, device=device())
+    assert tern.matmul(x1, w0, s0).shape == (2, 0)
+
+
+def test_rejects_misaligned_and_leaves_output_untouched():
+    base = torch.ones((1, 257), dtype=torch.float16, device=device())
+    x = base[:, 1:]                        # 2-byte offset: not 16-byte aligned
+    w = torch.zeros((8, 64), dtype=torch.uint8, device=device())
+    s = torch.ones((8, 2), dtype=torch.float16, device=device())
+    y = torch.full((1, 8), 3.0, dtype=torch.float32, device=device())
+    with pytest.raises(tern.TernError) as e:
+        tern.matmul_into(x, w, s, y)
+    assert e.value.status == 5
+    assert torch.all(y == 3.0).item()
+
+
+def test_multiple_calls_on_a_side_stream():
+    p = workloads.make_custom(900, 2, 1024, 300, x_dtype="f16", y_dtype="f32")
+    x, w, s = problem_to_device(p)
+    ref = tern.matmul(x, w, s, out_dtype=torch.float32).cpu()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        outs = [tern.matmul(x, w, s, out_dtype=torch.float32) for _ in range(4)]
+    st.synchronize()
+    for o in outs:
+        assert torch.equal(o.cpu(), ref)
