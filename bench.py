@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure the per-launch floor (a one-element kernel) and plain copy bandwidth")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each step from Python instead of replaying a captured HIP graph")
     return ap.parse_args()
 
 
@@ -69,8 +73,50 @@ def cpu_baseline(p, seconds: float):
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle", "sample": sample}
 
 
+def calibrate(steps: int):
+    """Per-launch floor and achievable bandwidth of plain torch kernels, same timing protocol."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    out = {"calibration": True}
+    one = torch.zeros(1, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            one.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    out["one_element_kernel_us_per_launch_graph"] = round(a.elapsed_time(b) * 1e3 / steps, 4)
+    for gb in (0.0066, 0.0223, 1.0):
+        n = int(gb * 1e9) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        reps = 20 if gb >= 1 else 200
+        copies = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(max(1, int(2.0 / gb)) if gb < 1 else 1)]
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            dst.copy_(copies[i % len(copies)])
+        b.record()
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) / 1e3 / reps
+        out[f"copy_{gb:g}GB_read_plus_write_GBps"] = round(2 * n * 4 / sec / 1e9, 1)
+        out[f"copy_{gb:g}GB_us"] = round(sec * 1e6, 3)
+        del copies
+    return out
+
+
 def main():
     args = parse()
+    if args.calibrate:
+        print(json.dumps(calibrate(args.steps)), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -107,13 +153,30 @@ def main():
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    if args.eager:
+        t_wall = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        end.record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+    else:
+        # The K timed steps are captured once into a HIP graph (a decode loop's
+        # launches, as a serving loop would replay them) and replayed once, so
+        # host launch overhead stays out of the measurement.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        graph.replay()                      # untimed replay: first-touch effects
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
     sec = ms_step / 1e3
@@ -152,7 +215,8 @@ def main():
         "config": {"workload": f"{cfg.name}: M={sh.M} K={sh.K} N={sh.N} ({sh.label})",
                    "M": sh.M, "K": sh.K, "N": sh.N, "group": 128, "x_dtype": p.x_dtype,
                    "y_dtype": p.y_dtype, "path": args.path, "weight_copies": copies,
-                   "rotated_bytes": int(copies * wbytes), "parallelism": "single GPU"},
+                   "rotated_bytes": int(copies * wbytes), "parallelism": "single GPU",
+                   "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roof,
         "packed_weight_bytes": int(packed_bytes),
         "algorithmic_bytes": int(alg_bytes),

@@ -11,7 +11,7 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxK = int64_t(1) << 30;
 constexpr int64_t kMaxProduct = int64_t(1) << 62;
-constexpr size_t kGemvLdsLimit = 96 * 1024;
+constexpr size_t kGemvLdsLimit = 152 * 1024;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

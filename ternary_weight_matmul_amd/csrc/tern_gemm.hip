@@ -88,21 +88,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 
     // activation prefetch registers
     uint4 a_reg[A_UNITS][2];
+    // Loads are unconditional at clamped, in-bounds addresses: rows past M
+    // and columns past N produce outputs that are never stored.  (A
+    // conditional load with a zeroing else-branch would make every load wait
+    // for the previous one.)
     auto load_a = [&](int kb) {
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
             const int b = tid + 256 * u;
             const int row = b >> 3;
             const int blk = b & 7;
-            const int m = m0 + row;
-            if (m < M) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (int64_t)kb * BK + blk * 16);
-                a_reg[u][0] = src[0];
-                a_reg[u][1] = src[1];
-            } else {
-                a_reg[u][0] = make_uint4(0, 0, 0, 0);
-                a_reg[u][1] = make_uint4(0, 0, 0, 0);
-            }
+            const int64_t m = min(m0 + row, M - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(X + m * K + (int64_t)kb * BK + blk * 16);
+            a_reg[u][0] = src[0];
+            a_reg[u][1] = src[1];
         }
     };
     auto store_a = [&]() {
@@ -125,14 +124,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     auto load_w = [&](int kb) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int n = n0 + nb * 16 + li;
-            if (n < N) {
-                w_reg[nb] = *reinterpret_cast<const uint2 *>(P + (int64_t)n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
-                s_reg[nb] = S[(int64_t)n * groups + kb];
-            } else {
-                w_reg[nb] = make_uint2(0, 0);
-                s_reg[nb] = 0;
-            }
+            const int64_t n = min(n0 + nb * 16 + li, N - 1);
+            w_reg[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
+            s_reg[nb] = S[n * groups + kb];
         }
     };
 

@@ -4,21 +4,25 @@
 // inside a 128-weight block the signs are accumulated with add / subtract /
 // skip and the block sum is multiplied by its fp16 scale at the block
 // boundary (§1.1, §4.1 third route, §4.2); activations and scales are kept
-// on chip, never re-read from memory in the inner loop (§4.2, §4.3).
+// on chip, never re-read from memory in the inner loop (§4.2, §4.3); wide
+// vector loads of the packed bytes (§4.3, third version).
 //
 // Work layout (one workgroup = 16 output rows x all of K):
-//   * a wave "step" covers 4 rows x 1024 weights per load instruction:
-//     lane = 16*r + kk; lane kk of row-group r loads 16 bytes (64 weights) of
-//     row n0 + 4j + r (j = 0..3) at K offset step*1024 + 64*kk.  Each load
-//     instruction reads four 256-byte contiguous row segments.
-//   * the waves of the workgroup split the K steps; each wave keeps one fp32
-//     partial per (row, m) per lane, reduces it over the 16 lanes of its DPP
-//     row, and the waves' partials are summed through LDS in a fixed order
-//     (deterministic; no atomics, no workspace).
-//   * X is staged once per workgroup into LDS, pair-interleaved (see
-//     tern_device.h) and swizzled so that the 16 lanes of a row-group read 16
-//     consecutive 16-byte pieces (conflict-free; the 4 row-groups broadcast).
+//   * a wave "step" covers 16 rows x 1024 weights: lane = 16*r + kk; for
+//     j = 0..3 the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
+//     offset step*1024 + 64*kk, so every load instruction reads four
+//     256-byte contiguous row segments;
+//   * the (at most 8) waves of a workgroup split the K steps.  Each wave first issues all
+//     of its weight and scale loads, then stages the activations of its own
+//     steps into a wave-private LDS slice (pair-interleaved, see
+//     tern_device.h; the four lanes that share a 64-weight chunk stage a
+//     quarter each), then decodes and accumulates as the loads land;
+//   * each lane keeps one fp32 partial per (row, m); it is summed over the
+//     16 lanes of its DPP row, then across the waves through LDS in a fixed
+//     order (deterministic; no atomics, no workspace).
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 
 #include "tern_device.h"
 #include "tern_kernels.h"
@@ -30,24 +34,37 @@ namespace {
 constexpr int ROWS = 16;          // output rows per workgroup
 constexpr int STEP = 1024;        // weights of one row per wave step
 constexpr int CHUNK = 64;         // weights per lane per row per step (16 bytes)
+constexpr int PIECES = 128;       // 16-byte activation pieces per (step, m): 16 chunks x 8
 
-// LDS word offset (in 16-byte pieces) of piece q (0..7) of 64-weight chunk c
-// of activation row m.
-__device__ __forceinline__ int x_piece(int m, int c, int q, int pieces_per_row) {
-    return m * pieces_per_row + ((c >> 4) * 8 + q) * 16 + (c & 15);
+// Sums of 2t*x over one lane's 64 weights (one 16-byte code vector) against
+// the pair-interleaved activation pieces xq[m][0..7] of the same chunk, for
+// every activation row m: each decoded pair feeds M packed dots.
+template <int M, bool BF16>
+__device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M][8], float (&part)[M]) {
+    constexpr uint32_t MASK = 0xC000C000u;
+    uint32_t v[4] = {code.x, code.y, code.z, code.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = sign_nz_fields(v[d]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = i >> 2;
+        const int e = i & 3;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t p = (v[d] << (14 - 2 * i)) & MASK;   // weights i and i+8 of word d
+#pragma unroll
+            for (int m = 0; m < M; ++m) part[m] = dot2<BF16>(p, (&xq[m][2 * d + q].x)[e], part[m]);
+        }
+    }
 }
 
-template <int M, bool XBF16, int YT>
-__global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ X,
+template <int M, bool XBF16, int YT, int SPW>
+__global__ __launch_bounds__(512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
-                                                     void *__restrict__ Y, int N, int K,
-                                                     int steps_per_wave) {
+                                                     void *__restrict__ Y, int N, int K) {
     extern __shared__ uint4 lds[];
     const int nsteps = (K + STEP - 1) / STEP;
-    const int pieces_per_row = nsteps * 128;  // 16 chunks x 8 pieces per step
-    float *red = reinterpret_cast<float *>(lds + M * pieces_per_row);
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -57,93 +74,96 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     const int n0 = blockIdx.x * ROWS;
     const int64_t row_bytes = K >> 2;
     const int groups = K >> 7;
+    uint4 *xw = lds + wave * (SPW * M * PIECES);                          // this wave's activations
+    float *red = reinterpret_cast<float *>(lds + nwaves * (SPW * M * PIECES));
 
-    // ---- this wave's weight loads go out first (they are the long pole) ----
-    const int s_begin = wave * steps_per_wave;
-    const int s_end = min(nsteps, s_begin + steps_per_wave);
+    const int s_begin = wave * SPW;
 
-    // ---- stage X into LDS: one 16-element block per thread iteration ----
-    const int blocks_per_row = K >> 4;
-    for (int b = tid; b < M * blocks_per_row; b += blockDim.x) {
-        const int m = b / blocks_per_row;
-        const int d = b - m * blocks_per_row;  // 16-element block along K
-        const uint4 *src = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (int64_t)d * 16);
-        const uint4 lo = src[0];
-        const uint4 hi = src[1];
-        uint32_t pr[8];
-        interleave16(lo, hi, pr);
-        const int c = d >> 2;              // 64-weight chunk
-        const int q0 = (d & 3) * 2;        // first of its two 16-byte pieces
-        lds[x_piece(m, c, q0, pieces_per_row)] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-        lds[x_piece(m, c, q0 + 1, pieces_per_row)] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+    // ---- 1. activation loads first (they gate the staging), then every
+    //         weight and scale load of this wave.  All loads are issued
+    //         unconditionally at clamped, in-bounds addresses: a row past N is
+    //         never stored, and a chunk past K is excluded when accumulating.
+    //         (A conditional load with a zeroing else-branch would force a
+    //         wait for every load before the next one is issued.)
+    const int nchunks = K / CHUNK;
+    uint4 xraw[SPW][M][2];
+#pragma unroll
+    for (int si = 0; si < SPW; ++si) {
+        const int c = min((s_begin + si) * 16 + kk, nchunks - 1);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            // lane (r, kk) fetches 16-element block r of chunk c
+            const uint4 *src = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (int64_t)c * CHUNK + r * 16);
+            xraw[si][m][0] = src[0];
+            xraw[si][m][1] = src[1];
+        }
     }
-    __syncthreads();
+    uint4 code[SPW][4];
+    uint32_t sbits[SPW][4];
+#pragma unroll
+    for (int si = 0; si < SPW; ++si) {
+        const int c = min((s_begin + si) * 16 + kk, nchunks - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = min(n0 + 4 * j + r, N - 1);
+            code[si][j] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
+            sbits[si][j] = S[n * groups + (c >> 1)];
+        }
+    }
 
+    // ---- 2. stage this wave's activations, pair-interleaved ----
+#pragma unroll
+    for (int si = 0; si < SPW; ++si) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            uint32_t pr[8];
+            interleave16(xraw[si][m][0], xraw[si][m][1], pr);
+            uint4 *dst = xw + (si * M + m) * PIECES;
+            dst[(2 * r) * 16 + kk] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+            dst[(2 * r + 1) * 16 + kk] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+        }
+    }
+    // the slice is private to this wave: a wave-level fence and barrier suffice
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 3. decode + sign-select accumulate, scale at the block boundary ----
     float acc[4][M];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
 
-    for (int s = s_begin; s < s_end; ++s) {
-        const int c = s * 16 + kk;                 // this lane's 64-weight chunk
-        const bool kact = c * CHUNK < K;
-        uint4 code[4];
-        float sc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + 4 * j + r;
-            if (kact && n < N) {
-                code[j] = *reinterpret_cast<const uint4 *>(P + (int64_t)n * row_bytes + (int64_t)c * 16);
-                sc[j] = f16_bits_to_float(S[(int64_t)n * groups + (c >> 1)]) * 0.5f;
-            } else {
-                code[j] = make_uint4(0, 0, 0, 0);
-                sc[j] = 0.f;
-            }
-        }
-        if (!kact) continue;
+    for (int si = 0; si < SPW; ++si) {
+        const bool kact = (s_begin + si) * 16 + kk < nchunks;   // this lane's chunk lies inside K
         uint4 xq[M][8];
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m) {
+            const uint4 *src = xw + (si * M + m) * PIECES;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) xq[m][q] = lds[x_piece(m, c, q, pieces_per_row)];
-
+            for (int q = 0; q < 8; ++q) xq[m][q] = src[q * 16 + kk];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            // this lane's 64 weights lie inside one 128-weight block; the +-2
+            // operands double the sum and the 0.5 undoes it exactly
             float part[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) part[m] = 0.f;
-            const uint32_t cw[4] = {code[j].x, code[j].y, code[j].z, code[j].w};
+            chunk_dot<M, XBF16>(code[si][j], xq, part);
+            const float s = f16_bits_to_float((uint16_t)sbits[si][j]) * 0.5f;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t v = sign_nz_fields(cw[d]);
-                const uint32_t p0 = weight_pair<0>(v), p1 = weight_pair<1>(v);
-                const uint32_t p2 = weight_pair<2>(v), p3 = weight_pair<3>(v);
-                const uint32_t p4 = weight_pair<4>(v), p5 = weight_pair<5>(v);
-                const uint32_t p6 = weight_pair<6>(v), p7 = weight_pair<7>(v);
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const uint4 a = xq[m][2 * d];
-                    const uint4 b = xq[m][2 * d + 1];
-                    float t = part[m];
-                    t = dot2<XBF16>(p0, a.x, t);
-                    t = dot2<XBF16>(p1, a.y, t);
-                    t = dot2<XBF16>(p2, a.z, t);
-                    t = dot2<XBF16>(p3, a.w, t);
-                    t = dot2<XBF16>(p4, b.x, t);
-                    t = dot2<XBF16>(p5, b.y, t);
-                    t = dot2<XBF16>(p6, b.z, t);
-                    t = dot2<XBF16>(p7, b.w, t);
-                    part[m] = t;
-                }
-            }
-            // block boundary: this lane's 64 weights lie in one 128-block
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[j][m] = fmaf(sc[j], part[m], acc[j][m]);
+            for (int m = 0; m < M; ++m) acc[j][m] = kact ? fmaf(s, part[m], acc[j][m]) : acc[j][m];
+            if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);   // one row's pairs live at a time
         }
+        // keep the scheduler from hoisting the next step's LDS reads into this
+        // step (that would hold several steps' activations in registers)
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- reduce over the 16 lanes of each DPP row, then across waves ----
+    // ---- 4. reduce over the 16 lanes of each DPP row, then across waves ----
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -165,31 +185,63 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     }
 }
 
-template <int M, bool XBF16, int YT>
-hipError_t launch_gemv_t(const GemmArgs &a) {
-    const int nsteps = (int)((a.K + STEP - 1) / STEP);
-    const int spw = (nsteps + 15) / 16;
-    const int nwaves = (nsteps + spw - 1) / spw;
-    const size_t lds_bytes = (size_t)M * nsteps * 128 * 16 + (size_t)nwaves * ROWS * M * sizeof(float);
-    auto kern = gemv_kernel<M, XBF16, YT>;
-    if (lds_bytes > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+struct GemvShape {
+    int nsteps, spw, nwaves;
+    size_t lds;
+};
+
+GemvShape gemv_shape(int64_t M, int64_t K) {
+    GemvShape g;
+    g.nsteps = (int)((K + STEP - 1) / STEP);
+    g.spw = (g.nsteps + 7) / 8;            // at most 8 waves per workgroup
+    if (g.spw < 1) g.spw = 1;
+    g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
+    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * ROWS * M * sizeof(float);
+    return g;
+}
+
+template <int M, bool XBF16, int YT, int SPW>
+hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
+    auto kern = gemv_kernel<M, XBF16, YT, SPW>;
+    if (g.lds > 64 * 1024) {
+        // raise the dynamic-LDS limit once per device (not a stream operation,
+        // so it is kept out of any graph capture after the first call)
+        static std::atomic<uint64_t> done_mask{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
+        const uint64_t bit = 1ull << (dev & 63);
+        if (!(done_mask.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            done_mask.fetch_or(bit, std::memory_order_acq_rel);
+        }
     }
     const dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
-    const dim3 block((unsigned)(64 * nwaves));
-    hipLaunchKernelGGL(kern, grid, block, lds_bytes, a.stream, static_cast<const uint16_t *>(a.X),
-                       a.W, a.S, a.Y, (int)a.N, (int)a.K, spw);
+    const dim3 block((unsigned)(64 * g.nwaves));
+    hipLaunchKernelGGL(kern, grid, block, g.lds, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S,
+                       a.Y, (int)a.N, (int)a.K);
     return hipGetLastError();
+}
+
+template <int M, bool XBF16, int YT>
+hipError_t launch_gemv_s(const GemmArgs &a) {
+    const GemvShape g = gemv_shape(M, a.K);
+    switch (g.spw) {
+    case 1: return launch_gemv_t<M, XBF16, YT, 1>(a, g);
+    case 2: return launch_gemv_t<M, XBF16, YT, 2>(a, g);
+    case 3: return launch_gemv_t<M, XBF16, YT, 3>(a, g);
+    default: return launch_gemv_t<M, XBF16, YT, 4>(a, g);
+    }
 }
 
 template <int M, bool XBF16>
 hipError_t launch_gemv_y(const GemmArgs &a) {
     switch (a.y_dtype) {
-    case 0: return launch_gemv_t<M, XBF16, 0>(a);
-    case 1: return launch_gemv_t<M, XBF16, 1>(a);
-    default: return launch_gemv_t<M, XBF16, 2>(a);
+    case 0: return launch_gemv_s<M, XBF16, 0>(a);
+    case 1: return launch_gemv_s<M, XBF16, 1>(a);
+    default: return launch_gemv_s<M, XBF16, 2>(a);
     }
 }
 
@@ -201,10 +253,9 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) {
-    const int64_t nsteps = (K + STEP - 1) / STEP;
-    const int64_t spw = (nsteps + 15) / 16;
-    const int64_t nwaves = (nsteps + spw - 1) / spw;
-    return (size_t)(M * nsteps * 128 * 16 + nwaves * ROWS * M * 4);
+    const GemvShape g = gemv_shape(M, K);
+    if (g.spw > 4) return (size_t)-1;   // K > 32768: more than four steps per wave, not this kernel
+    return g.lds;
 }
 
 hipError_t launch_gemv(const GemmArgs &a) {

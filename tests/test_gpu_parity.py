@@ -270,3 +270,24 @@ def test_multiple_calls_on_a_side_stream():
     st.synchronize()
     for o in outs:
         assert torch.equal(o.cpu(), ref)
+
+
+@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 5120, 640, "bf16", "bf16"), (2, 17408, 96, "bf16", "f32"),
+                                         (300, 1024, 512, "f16", "f16")])
+def test_hip_graph_replays_match_eager(M, K, N, xd, yd):
+    """Captured launches replay to the eager result, every time."""
+    p = workloads.make_custom(700 + M, M, K, N, x_dtype=xd, y_dtype=yd)
+    x, w, s = problem_to_device(p)
+    eager = tern.matmul(x, w, s, out_dtype=TORCH_DT[yd]).clone()
+    y = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tern.matmul_into(x, w, s, y)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16 if yd != "f32" else torch.int32),
+                           eager.view(torch.int16 if yd != "f32" else torch.int32)), rep
+        tern.matmul(x, w, s, out_dtype=TORCH_DT[yd])   # eager work between replays
