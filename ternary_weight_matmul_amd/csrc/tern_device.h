@@ -35,6 +35,41 @@ __device__ __forceinline__ uint32_t sign_nz_fields(uint32_t w) {
     return w ^ ((w >> 1) & 0x55555555u);
 }
 
+// 64-bit shifts of a register pair.  On gfx950 v_lshlrev_b64 issues at the
+// same rate as a 32-bit shift, so one instruction moves the fields of two
+// code words; the compiler would split it into two 32-bit operations.
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+    if constexpr (S == 0) {
+        return v;
+    } else {
+        uint64_t r;
+        asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(v));
+        return r;
+    }
+}
+__device__ __forceinline__ uint64_t shr64_1(uint64_t v) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, 1, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Field transform of two code words at once (bits that cross between the
+// words are cleared by the 0x5555... mask).
+__device__ __forceinline__ uint64_t sign_nz_fields64(uint64_t w) {
+    return w ^ (shr64_1(w) & 0x5555555555555555ull);
+}
+
+// +-2 / 0 pairs for weights (i, i+8) of both words of a transformed pair:
+// after a 64-bit shift by 14 - 2i, the bits that cross from the low word
+// into the high word land below bit 14 and are masked away.
+template <int I>
+__device__ __forceinline__ void weight_pairs2(uint64_t v, uint32_t &lo, uint32_t &hi) {
+    const uint64_t t = shl64<14 - 2 * I>(v);
+    lo = (uint32_t)t & 0xC000C000u;
+    hi = (uint32_t)(t >> 32) & 0xC000C000u;
+}
+
 // +-2 / 0 pair for weights (i, i+8) of a transformed word.
 template <int I>
 __device__ __forceinline__ uint32_t weight_pair(uint32_t v) {

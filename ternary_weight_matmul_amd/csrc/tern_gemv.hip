@@ -12,7 +12,7 @@
 //     j = 0..3 the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
 //     offset step*1024 + 64*kk, so every load instruction reads four
 //     256-byte contiguous row segments;
-//   * the (at most 8) waves of a workgroup split the K steps.  Each wave first issues all
+//   * the waves of a workgroup (up to 16 for M = 1, 8 otherwise) split the K steps.  Each wave first issues all
 //     of its weight and scale loads, then stages the activations of its own
 //     steps into a wave-private LDS slice (pair-interleaved, see
 //     tern_device.h; the four lanes that share a 64-weight chunk stage a
@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "tern_device.h"
 #include "tern_kernels.h"
@@ -41,25 +42,35 @@ constexpr int PIECES = 128;       // 16-byte activation pieces per (step, m): 16
 // every activation row m: each decoded pair feeds M packed dots.
 template <int M, bool BF16>
 __device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M][8], float (&part)[M]) {
-    constexpr uint32_t MASK = 0xC000C000u;
-    uint32_t v[4] = {code.x, code.y, code.z, code.w};
+    const uint64_t a = sign_nz_fields64((uint64_t)code.x | ((uint64_t)code.y << 32));
+    const uint64_t b = sign_nz_fields64((uint64_t)code.z | ((uint64_t)code.w << 32));
+    auto step = [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        constexpr int q = I >> 2;
+        constexpr int e = I & 3;
+        uint32_t p0, p1, p2, p3;
+        weight_pairs2<I>(a, p0, p1);   // words 0, 1
+        weight_pairs2<I>(b, p2, p3);   // words 2, 3
 #pragma unroll
-    for (int d = 0; d < 4; ++d) v[d] = sign_nz_fields(v[d]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = i >> 2;
-        const int e = i & 3;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t p = (v[d] << (14 - 2 * i)) & MASK;   // weights i and i+8 of word d
-#pragma unroll
-            for (int m = 0; m < M; ++m) part[m] = dot2<BF16>(p, (&xq[m][2 * d + q].x)[e], part[m]);
+        for (int m = 0; m < M; ++m) {
+            part[m] = dot2<BF16>(p0, (&xq[m][0 + q].x)[e], part[m]);
+            part[m] = dot2<BF16>(p1, (&xq[m][2 + q].x)[e], part[m]);
+            part[m] = dot2<BF16>(p2, (&xq[m][4 + q].x)[e], part[m]);
+            part[m] = dot2<BF16>(p3, (&xq[m][6 + q].x)[e], part[m]);
         }
-    }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
 }
 
 template <int M, bool XBF16, int YT, int SPW>
-__global__ __launch_bounds__(512) void gemv_kernel(const uint16_t *__restrict__ X,
+__global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
                                                      void *__restrict__ Y, int N, int K) {
@@ -135,28 +146,36 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint16_t *__restrict__ 
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
 
+    // activation rows are taken one at a time (a row's 32 activation words in
+    // registers); for M > 1 each code word is decoded once per row, which
+    // keeps the register footprint of M = 1
+    constexpr int MC = 1;
 #pragma unroll
     for (int si = 0; si < SPW; ++si) {
         const bool kact = (s_begin + si) * 16 + kk < nchunks;   // this lane's chunk lies inside K
-        uint4 xq[M][8];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint4 *src = xw + (si * M + m) * PIECES;
+        for (int mb = 0; mb < M; mb += MC) {
+            uint4 xq[MC][8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) xq[m][q] = src[q * 16 + kk];
-        }
+            for (int m = 0; m < MC; ++m) {
+                const uint4 *src = xw + (si * M + mb + m) * PIECES;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // this lane's 64 weights lie inside one 128-weight block; the +-2
-            // operands double the sum and the 0.5 undoes it exactly
-            float part[M];
+                for (int q = 0; q < 8; ++q) xq[m][q] = src[q * 16 + kk];
+            }
 #pragma unroll
-            for (int m = 0; m < M; ++m) part[m] = 0.f;
-            chunk_dot<M, XBF16>(code[si][j], xq, part);
-            const float s = f16_bits_to_float((uint16_t)sbits[si][j]) * 0.5f;
+            for (int j = 0; j < 4; ++j) {
+                // this lane's 64 weights lie inside one 128-weight block; the +-2
+                // operands double the sum and the 0.5 undoes it exactly
+                float part[MC];
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[j][m] = kact ? fmaf(s, part[m], acc[j][m]) : acc[j][m];
-            if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);   // one row's pairs live at a time
+                for (int m = 0; m < MC; ++m) part[m] = 0.f;
+                chunk_dot<MC, XBF16>(code[si][j], xq, part);
+                const float s = f16_bits_to_float((uint16_t)sbits[si][j]) * 0.5f;
+#pragma unroll
+                for (int m = 0; m < MC; ++m)
+                    acc[j][mb + m] = kact ? fmaf(s, part[m], acc[j][mb + m]) : acc[j][mb + m];
+                if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);   // one row's pairs live at a time
+            }
         }
         // keep the scheduler from hoisting the next step's LDS reads into this
         // step (that would hold several steps' activations in registers)
@@ -193,7 +212,8 @@ struct GemvShape {
 GemvShape gemv_shape(int64_t M, int64_t K) {
     GemvShape g;
     g.nsteps = (int)((K + STEP - 1) / STEP);
-    g.spw = (g.nsteps + 7) / 8;            // at most 8 waves per workgroup
+    const int max_waves = M == 1 ? 16 : 8;  // (M > 1 needs the 256-register budget of <= 512 threads)
+    g.spw = (g.nsteps + max_waves - 1) / max_waves;
     if (g.spw < 1) g.spw = 1;
     g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
     g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * ROWS * M * sizeof(float);
@@ -254,7 +274,9 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) {
     const GemvShape g = gemv_shape(M, K);
-    if (g.spw > 4) return (size_t)-1;   // K > 32768: more than four steps per wave, not this kernel
+    // more steps per wave than the register budget holds (M = 1: K > 32768;
+    // M > 1: K > 32768 as well, with 8 waves of up to 4 steps): not this kernel
+    if (g.spw > (M == 1 ? 2 : 4)) return (size_t)-1;
     return g.lds;
 }
 
