@@ -7,21 +7,30 @@
 // matrix cores, because with many activation rows the work is a dense
 // contraction.
 //
-// Tiling: a workgroup of 4 waves computes a (16*MB) x 256 tile of Y; wave w
-// owns columns 64w..64w+63 (4 blocks of 16) and all 16*MB rows.  Per
-// 128-wide K block (one scale group):
-//   * X[rows, 128] goes global -> registers -> LDS, pair-interleaved (see
-//     tern_device.h), row stride 272 bytes (bank-conflict-free 16-byte reads);
-//   * each lane loads 8 bytes of codes (32 weights) for each of its 4
-//     columns and decodes them in registers straight into MFMA B operands:
-//     +-2 pairs (tern_device.h); with fp16 X they are multiplied by the fp16
-//     scale (+-2s, exact); with bf16 X they stay +-2 and the scale is applied
-//     in fp32 to the block's partial sum;
+// Tiling.  A workgroup has WN x WK waves and computes a (16*MB) x (16*NB*WN)
+// tile of Y.  Wave (wn, wk) owns columns 16*NB*wn .. +16*NB of the tile and
+// the K blocks kb = it*WK + wk (128-wide, one scale group each); with WK > 1
+// the waves' partial tiles are summed through LDS at the end (fixed order).
+// Per iteration:
+//   * X[rows, WK K blocks] goes global -> registers -> LDS, pair-interleaved
+//     (tern_device.h), 272-byte padded rows (16-byte reads without bank
+//     conflicts); the LDS tile is double-buffered (one barrier per iteration)
+//     and the global loads run two iterations ahead;
+//   * each lane loads 8 code bytes (32 weights) of its column for each of its
+//     NB column blocks (prefetched two iterations ahead) and decodes them in
+//     registers straight into MFMA B operands: +-2 pairs (tern_device.h);
+//     with fp16 X they are multiplied by the fp16 scale (+-2s, exact); with
+//     bf16 X they stay +-2 and the block's fp32 partial sum is scaled;
 //   * v_mfma_f32_16x16x32_{f16,bf16}: lane l gives A[l%16][8(l/16)+e] and
-//     B[8(l/16)+e][l%16]; the lane's 32 weights of a block are spread over
-//     the 4 MFMA k-steps so that the activation fragment for step t is the
-//     16-byte run X'[32g + 8t .. +8] of the pair-interleaved row.
+//     B[8(l/16)+e][l%16]; the lane's 32 weights of a block are spread over the
+//     4 MFMA k-steps so that the activation fragment of step t is the 16-byte
+//     run X'[32g + 8t .. +8] of the pair-interleaved row.
+// Workgroups are numbered so that each XCD (workgroups go round-robin over
+// the 8 XCDs) gets a contiguous run of tiles, which share activation rows in
+// that XCD's L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "tern_device.h"
 #include "tern_kernels.h"
@@ -34,9 +43,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 256;              // columns per workgroup
-constexpr int NB = 4;                // 16-column blocks per wave
-constexpr int BK = 128;              // K per iteration (= one scale group)
+constexpr int BK = 128;              // K per block (= one scale group)
 constexpr int LDS_ROW = 272;         // bytes per staged activation row (256 + 16 pad)
 
 template <bool BF16>
@@ -54,79 +61,85 @@ __device__ __forceinline__ uint32_t mul_pair_f16(uint32_t p, half2_t s2) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) * s2);
 }
 
-// The 4 B-operand words for k-step t from one lane's 8 code bytes.
-template <int T>
-__device__ __forceinline__ uint4 b_operand(uint32_t v_lo, uint32_t v_hi) {
-    const uint32_t v = (T < 2) ? v_lo : v_hi;
-    constexpr int H = T & 1;
-    return make_uint4(weight_pair<4 * H + 0>(v), weight_pair<4 * H + 1>(v),
-                      weight_pair<4 * H + 2>(v), weight_pair<4 * H + 3>(v));
-}
-
-template <int MB, bool XBF16, int YT>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ X,
-                                                    const uint8_t *__restrict__ P,
-                                                    const uint16_t *__restrict__ S,
-                                                    void *__restrict__ Y, int M, int N, int K,
-                                                    int tiles_n) {
+template <int MB, int NB, int WN, int WK, bool XBF16, int YT>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ X,
+                                                             const uint8_t *__restrict__ P,
+                                                             const uint16_t *__restrict__ S,
+                                                             void *__restrict__ Y, int M, int N, int K,
+                                                             int tiles_m, int tiles_n) {
     constexpr int BM = 16 * MB;
-    constexpr int A_UNITS = BM * (BK / 16) / 256;   // 16-element blocks per thread per K block
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[BM * LDS_ROW];
+    constexpr int BN = 16 * NB * WN;
+    constexpr int NT = 64 * WN * WK;
+    constexpr int A_UNITS_TOTAL = WK * BM * (BK / 16);   // 16-element units per iteration
+    constexpr int A_UNITS = (A_UNITS_TOTAL + NT - 1) / NT;
+    constexpr int A_TILE = BM * LDS_ROW;                  // bytes of one K block's activations
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * WK * A_TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wn = wave % WN;
+    const int wk = wave / WN;
     const int li = lane & 15;   // row (A) / column (B) within a 16-block
     const int lg = lane >> 4;   // k-slot group
-    const int tile_m = blockIdx.x / tiles_n;
-    const int tile_n = blockIdx.x - tile_m * tiles_n;
+
+    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+    // contiguous range of tiles (tile_n fastest), so neighbours share rows.
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
+    const int tile_m = tile / tiles_n;
+    const int tile_n = tile - tile_m * tiles_n;
     const int m0 = tile_m * BM;
-    const int n0 = tile_n * BN + wave * 64;
+    const int n0 = tile_n * BN + wn * (16 * NB);
     const int64_t row_bytes = K >> 2;
     const int groups = K >> 7;
-    const int nk = K / BK;
+    const int nkb = K / BK;
+    const int niter = (nkb + WK - 1) / WK;
 
-    // activation prefetch registers
+    // ---- activation tile: global -> registers (clamped, unconditional) ----
     uint4 a_reg[A_UNITS][2];
-    // Loads are unconditional at clamped, in-bounds addresses: rows past M
-    // and columns past N produce outputs that are never stored.  (A
-    // conditional load with a zeroing else-branch would make every load wait
-    // for the previous one.)
-    auto load_a = [&](int kb) {
+    auto load_a = [&](int it) {
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
-            const int b = tid + 256 * u;
-            const int row = b >> 3;
-            const int blk = b & 7;
+            const int b = min(tid + NT * u, A_UNITS_TOTAL - 1);
+            const int w = b / (BM * 8);              // which of the WK K blocks
+            const int rem = b - w * (BM * 8);
+            const int row = rem >> 3;
+            const int blk = rem & 7;
+            const int kb = min(it * WK + w, nkb - 1);
             const int64_t m = min(m0 + row, M - 1);
             const uint4 *src = reinterpret_cast<const uint4 *>(X + m * K + (int64_t)kb * BK + blk * 16);
             a_reg[u][0] = src[0];
             a_reg[u][1] = src[1];
         }
     };
-    auto store_a = [&]() {
+    auto store_a = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
-            const int b = tid + 256 * u;
-            const int row = b >> 3;
-            const int blk = b & 7;
-            uint32_t pr[8];
-            interleave16(a_reg[u][0], a_reg[u][1], pr);
-            uint4 *dst = reinterpret_cast<uint4 *>(a_lds + row * LDS_ROW + blk * 32);
-            dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-            dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+            const int b = tid + NT * u;
+            if (A_UNITS * NT == A_UNITS_TOTAL || b < A_UNITS_TOTAL) {
+                const int w = b / (BM * 8);
+                const int rem = b - w * (BM * 8);
+                const int row = rem >> 3;
+                const int blk = rem & 7;
+                uint32_t pr[8];
+                interleave16(a_reg[u][0], a_reg[u][1], pr);
+                uint4 *dst = reinterpret_cast<uint4 *>(a_lds + (buf * WK + w) * A_TILE + row * LDS_ROW + blk * 32);
+                dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+            }
         }
     };
 
-    // weight prefetch registers: 8 code bytes + one scale per column block
-    uint2 w_reg[NB];
-    uint16_t s_reg[NB];
-    auto load_w = [&](int kb) {
+    // ---- weights: 8 code bytes + one scale per column block (clamped) ----
+    auto load_w = [&](int it, uint2 (&w)[NB], uint32_t (&s)[NB]) {
+        const int kb = min(it * WK + wk, nkb - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int64_t n = min(n0 + nb * 16 + li, N - 1);
-            w_reg[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
-            s_reg[nb] = S[n * groups + kb];
+            w[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
+            s[nb] = S[n * groups + kb];
         }
     };
 
@@ -136,88 +149,139 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    uint2 w0[NB], w1[NB];
+    uint32_t s0[NB], s1[NB];
     load_a(0);
-    load_w(0);
-    for (int kb = 0; kb < nk; ++kb) {
-        __syncthreads();                 // everyone is done reading the previous tile
-        store_a();
-        __syncthreads();
-        uint2 w_cur[NB];
-        uint16_t s_cur[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            w_cur[nb] = w_reg[nb];
-            s_cur[nb] = s_reg[nb];
-        }
-        if (kb + 1 < nk) {               // next block's loads overlap this block's math
-            load_a(kb + 1);
-            load_w(kb + 1);
-        }
+    load_w(0, w0, s0);
+    store_a(0);
+    if (niter > 1) {
+        load_a(1);
+        load_w(1, w1, s1);
+    }
+    __syncthreads();
 
-        uint32_t v_lo[NB], v_hi[NB];
+    for (int it = 0; it < niter; ++it) {
+        const int buf = it & 1;
+        if (it * WK + wk < nkb) {             // this wave's K block exists (uniform per wave)
+            // decode: field transform of the lane's two code words per column block
+            uint64_t v[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            v_lo[nb] = sign_nz_fields(w_cur[nb].x);
-            v_hi[nb] = sign_nz_fields(w_cur[nb].y);
-        }
+            for (int nb = 0; nb < NB; ++nb)
+                v[nb] = sign_nz_fields64((uint64_t)w0[nb].x | ((uint64_t)w0[nb].y << 32));
 
-        float4_t part[XBF16 ? MB : 1][XBF16 ? NB : 1];
-        if constexpr (XBF16) {
+            float4_t part[XBF16 ? MB : 1][XBF16 ? NB : 1];
+            if constexpr (XBF16) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
+                for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-        }
-
-        auto kstep = [&](auto tc) {
-            constexpr int T = decltype(tc)::value;
-            uint4 bop[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                uint4 b = b_operand<T>(v_lo[nb], v_hi[nb]);
-                if constexpr (!XBF16) {
-                    const _Float16 sh = __builtin_bit_cast(_Float16, s_cur[nb]);
-                    const half2_t s2 = {sh, sh};
-                    b.x = mul_pair_f16(b.x, s2);
-                    b.y = mul_pair_f16(b.y, s2);
-                    b.z = mul_pair_f16(b.z, s2);
-                    b.w = mul_pair_f16(b.w, s2);
-                }
-                bop[nb] = b;
+                    for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(a_lds + (mb * 16 + li) * LDS_ROW + (32 * lg + 8 * T) * 2);
+            const uint8_t *a_base = a_lds + (buf * WK + wk) * A_TILE + li * LDS_ROW + lg * 64;
+
+            // k-steps H and H+2 use pairs 4H..4H+3 of word 0 and of word 1:
+            // one 64-bit shift per pair index gives both (low and high half)
+            auto kstep2 = [&](auto hc) {
+                constexpr int H = decltype(hc)::value;
+                uint4 blo[NB], bhi[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    if constexpr (XBF16)
-                        part[mb][nb] = mfma16x16x32<true>(a, bop[nb], part[mb][nb]);
-                    else
-                        acc[mb][nb] = mfma16x16x32<false>(a, bop[nb], acc[mb][nb]);
+                    uint32_t lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+                    weight_pairs2<4 * H + 0>(v[nb], lo0, hi0);
+                    weight_pairs2<4 * H + 1>(v[nb], lo1, hi1);
+                    weight_pairs2<4 * H + 2>(v[nb], lo2, hi2);
+                    weight_pairs2<4 * H + 3>(v[nb], lo3, hi3);
+                    uint4 bl = make_uint4(lo0, lo1, lo2, lo3);
+                    uint4 bh = make_uint4(hi0, hi1, hi2, hi3);
+                    if constexpr (!XBF16) {
+                        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)s0[nb]);
+                        const half2_t s2 = {sh, sh};
+                        bl.x = mul_pair_f16(bl.x, s2);
+                        bl.y = mul_pair_f16(bl.y, s2);
+                        bl.z = mul_pair_f16(bl.z, s2);
+                        bl.w = mul_pair_f16(bl.w, s2);
+                        bh.x = mul_pair_f16(bh.x, s2);
+                        bh.y = mul_pair_f16(bh.y, s2);
+                        bh.z = mul_pair_f16(bh.z, s2);
+                        bh.w = mul_pair_f16(bh.w, s2);
+                    }
+                    blo[nb] = bl;
+                    bhi[nb] = bh;
                 }
-            }
-        };
-        kstep(std::integral_constant<int, 0>{});
-        kstep(std::integral_constant<int, 1>{});
-        kstep(std::integral_constant<int, 2>{});
-        kstep(std::integral_constant<int, 3>{});
-
-        if constexpr (XBF16) {           // block boundary: scale the block's sums
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float s = f16_bits_to_float(s_cur[nb]) * 0.5f;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
-                    acc[mb][nb][1] = fmaf(s, part[mb][nb][1], acc[mb][nb][1]);
-                    acc[mb][nb][2] = fmaf(s, part[mb][nb][2], acc[mb][nb][2]);
-                    acc[mb][nb][3] = fmaf(s, part[mb][nb][3], acc[mb][nb][3]);
+                    const uint8_t *arow = a_base + mb * 16 * LDS_ROW;
+                    const uint4 al = *reinterpret_cast<const uint4 *>(arow + H * 16);         // k-step H
+                    const uint4 ah = *reinterpret_cast<const uint4 *>(arow + (H + 2) * 16);   // k-step H+2
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        if constexpr (XBF16) {
+                            part[mb][nb] = mfma16x16x32<true>(al, blo[nb], part[mb][nb]);
+                            part[mb][nb] = mfma16x16x32<true>(ah, bhi[nb], part[mb][nb]);
+                        } else {
+                            acc[mb][nb] = mfma16x16x32<false>(al, blo[nb], acc[mb][nb]);
+                            acc[mb][nb] = mfma16x16x32<false>(ah, bhi[nb], acc[mb][nb]);
+                        }
+                    }
+                }
+            };
+            kstep2(std::integral_constant<int, 0>{});
+            kstep2(std::integral_constant<int, 1>{});
+
+            if constexpr (XBF16) {           // block boundary: scale the block's sums
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float s = f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
+                        acc[mb][nb][1] = fmaf(s, part[mb][nb][1], acc[mb][nb][1]);
+                        acc[mb][nb][2] = fmaf(s, part[mb][nb][2], acc[mb][nb][2]);
+                        acc[mb][nb][3] = fmaf(s, part[mb][nb][3], acc[mb][nb][3]);
+                    }
                 }
             }
+        }
+        // next tile into the other buffer; loads two iterations ahead
+        if (it + 1 < niter) store_a(buf ^ 1);
+        if (it + 2 < niter) load_a(it + 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            w0[nb] = w1[nb];
+            s0[nb] = s1[nb];
+        }
+        if (it + 2 < niter) load_w(it + 2, w1, s1);
+        __syncthreads();
+    }
+
+    // ---- waves that split K: sum their partial tiles through LDS ----
+    if constexpr (WK > 1) {
+        float *red = reinterpret_cast<float *>(a_lds);   // reuse the tile buffer
+        constexpr int PER_WAVE = MB * NB * 4 * 64;        // floats
+        static_assert((size_t)(WK - 1) * WN * PER_WAVE * 4 <= sizeof(a_lds), "reduction buffer");
+        if (wk > 0) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[(((wk - 1) * WN + wn) * MB * NB * 4 + (mb * NB + nb) * 4 + i) * 64 + lane] =
+                            acc[mb][nb][i];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+        for (int w = 1; w < WK; ++w) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[mb][nb][i] += red[(((w - 1) * WN + wn) * MB * NB * 4 + (mb * NB + nb) * 4 + i) * 64 + lane];
         }
     }
 
-    // epilogue: lane l holds rows 4(l/16)+i, column l%16 of each 16x16 block
+    // ---- epilogue: lane l holds rows 4(l/16)+i, column l%16 of each 16x16 block ----
     const float post = XBF16 ? 1.0f : 0.5f;    // the +-2s operand counted each weight twice
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -233,25 +297,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
         }
 }
 
-template <int MB, bool XBF16, int YT>
+template <int MB, int NB, int WN, int WK, bool XBF16, int YT>
 hipError_t launch_t(const GemmArgs &a) {
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
-    const int64_t tiles_m = (a.M + 16 * MB - 1) / (16 * MB);
+    const int64_t tiles_m = (a.M + BM - 1) / BM;
     if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(tiles_n * tiles_m));
-    hipLaunchKernelGGL((gemm_kernel<MB, XBF16, YT>), grid, dim3(256), 0, a.stream,
-                       static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y, (int)a.M, (int)a.N, (int)a.K,
-                       (int)tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XBF16, YT>), dim3((unsigned)(tiles_n * tiles_m)),
+                       dim3(64 * WN * WK), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y,
+                       (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
+}
+
+template <bool XBF16, int YT>
+hipError_t launch_shape(const GemmArgs &a) {
+    if (a.M <= 16) return launch_t<1, 2, 2, 4, XBF16, YT>(a);        // 16 x 64 tiles, K split over 4 waves
+    else return launch_t<4, 4, 4, 1, XBF16, YT>(a);                  // 64 x 256
 }
 
 template <bool XBF16>
 hipError_t launch_y(const GemmArgs &a) {
-    constexpr int MB = XBF16 ? 4 : 8;
     switch (a.y_dtype) {
-    case 0: return launch_t<MB, XBF16, 0>(a);
-    case 1: return launch_t<MB, XBF16, 1>(a);
-    default: return launch_t<MB, XBF16, 2>(a);
+    case 0: return launch_shape<XBF16, 0>(a);
+    case 1: return launch_shape<XBF16, 1>(a);
+    default: return launch_shape<XBF16, 2>(a);
     }
 }
 
