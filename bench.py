@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the per-launch floor (a one-element kernel) and plain copy bandwidth")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparison route, the other workloads and the decode sweep")
     ap.add_argument("--eager", action="store_true",
                     help="launch each step from Python instead of replaying a captured HIP graph")
     return ap.parse_args()
@@ -137,6 +139,156 @@ def calibrate(steps: int):
         out[f"copy_{gb:g}GB_us"] = round(sec * 1e6, 3)
         del copies
     return out
+
+
+def _tdt(name):
+    import torch
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def _device_problem(p, rotate_gb):
+    """Device copies of a problem: X, Y and enough weight copies to span rotate_gb."""
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    sh = p.shape
+    x = torch.from_numpy(p.x.view(np.int16)).to(dev).view(_tdt(p.x_dtype))
+    w0 = torch.from_numpy(p.packed).to(dev)
+    s0 = torch.from_numpy(p.scales.view(np.int16)).to(dev).view(torch.float16)
+    wbytes = w0.numel() + s0.numel() * 2
+    copies = max(1, int(np.ceil(rotate_gb * 1e9 / wbytes)))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    y = torch.empty((sh.M, sh.N), dtype=_tdt(p.y_dtype), device=dev)
+    return x, ws, ss, y, copies, wbytes
+
+
+def _graph_time_ms(step, steps, warmup):
+    """ms per step of `steps` calls captured in one HIP graph (after warm-up)."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(warmup + i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def _summary(p, ms):
+    sh = p.shape
+    sec = ms / 1e3
+    yb = {"f32": 4, "bf16": 2, "f16": 2}[p.y_dtype]
+    alg = sh.N * sh.K / 4 + sh.N * sh.K / 64 + 2 * sh.M * sh.K + yb * sh.M * sh.N
+    out = {"M": sh.M, "K": sh.K, "N": sh.N, "us_per_launch": round(ms * 1e3, 3),
+           "packed_GBps": round(sh.N * sh.K / 4 / sec / 1e9, 1),
+           "alg_GBps": round(alg / sec / 1e9, 1), "TFLOPs": round(2.0 * sh.M * sh.N * sh.K / sec / 1e12, 2)}
+    if sh.M <= 16:
+        out["roofline"] = {"bound": "hbm", "frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        out["roofline"] = {"bound": "mfma", "frac": round(2.0 * sh.M * sh.N * sh.K / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def other_workloads(skip):
+    """Every configured shape except the headline one, same protocol, fewer steps."""
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    res = []
+    for cid in (1, 2, 3, 4, 5):
+        for si, sh in enumerate(workloads.CONFIGS[cid].shapes):
+            if (cid, si) == skip:
+                continue
+            p = workloads.make_problem(cid, si)
+            x, ws, ss, y, copies, _ = _device_problem(p, 1.0)
+            big = sh.M * sh.N * sh.K > 1e10
+            steps = 40 if big else (200 if sh.M > 16 else 500)
+            ms = _graph_time_ms(lambda i: tern.matmul_into(x, ws[i % copies], ss[i % copies], y),
+                                steps, 10)
+            rec = {"workload": f"{workloads.CONFIGS[cid].name} ({sh.label})", **_summary(p, ms)}
+            res.append(rec)
+            del x, ws, ss, y
+            torch.cuda.empty_cache()
+    return res
+
+
+def comparison_route(cid, si):
+    """The pages' first route: dequantise to 16-bit W, then a library GEMM (hipBLASLt via
+    torch), against the fused kernel, on one workload (no weight rotation for either)."""
+    import numpy as np
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    p = workloads.make_problem(cid, si)
+    sh = p.shape
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(p.x.view(np.int16)).to(dev).view(_tdt(p.x_dtype))
+    w = torch.from_numpy(p.packed).to(dev)
+    s = torch.from_numpy(p.scales.view(np.int16)).to(dev).view(torch.float16)
+    wdt = _tdt(p.x_dtype)
+    W = torch.empty((sh.N, sh.K), dtype=wdt, device=dev)
+    xT = x.t().contiguous()                     # [K, M]: both GEMM operands contiguous
+    yT = torch.empty((sh.N, sh.M), dtype=wdt, device=dev)
+    y = torch.empty((sh.M, sh.N), dtype=_tdt(p.y_dtype), device=dev)
+    steps = 20 if sh.M > 16 else 200
+    t_deq = _graph_time_ms(lambda i: tern.dequant(w, s, out=W), steps, 5)
+    t_gemm = _graph_time_ms(lambda i: torch.matmul(W, xT, out=yT), steps, 5)
+    t_fused = _graph_time_ms(lambda i: tern.matmul_into(x, w, s, y), steps, 5)
+    return {"workload": f"{workloads.CONFIGS[cid].name} M={sh.M} K={sh.K} N={sh.N}",
+            "dequant_us": round(t_deq * 1e3, 3), "library_gemm_us": round(t_gemm * 1e3, 3),
+            "route_total_us": round((t_deq + t_gemm) * 1e3, 3), "fused_us": round(t_fused * 1e3, 3),
+            "route_over_fused": round((t_deq + t_gemm) / t_fused, 3),
+            "dense_weight_bytes": int(sh.N * sh.K * 2), "packed_weight_bytes": int(sh.N * sh.K // 4),
+            "note": "weights resident (no rotation) for both routes"}
+
+
+def decode_sweep(reps: int = 3):
+    """One token through 48 layers x 7 projections at M=1 (q, k, v, o 5120->5120; gate, up
+    5120->17408; down 17408->5120): 336 launches over distinct weights captured in one graph."""
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[6]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    xs = {k: torch.randn((1, k), generator=gen, device=dev).to(torch.bfloat16) for k in (5120, 17408)}
+    mats = []
+    packed_bytes = scale_bytes = 0
+    for sh in cfg.shapes:
+        w = workloads.draw_packed_device(gen, sh.N, sh.K, cfg.code_probs)
+        s = workloads.draw_scales_device(gen, sh.N, sh.K // 128, cfg.scale_lo, cfg.scale_hi)
+        y = torch.empty((1, sh.N), dtype=torch.bfloat16, device=dev)
+        mats.append((xs[sh.K], w, s, y))
+        packed_bytes += w.numel()
+        scale_bytes += s.numel() * 2
+    n = len(mats)
+    ms = _graph_time_ms(lambda i: tern.matmul_into(*mats[i % n]), n * reps, n) * n
+    tok_s = 1e3 / ms
+    return {"workload": "decode sweep: 48 layers x 7 projections, M=1, bf16",
+            "launches_per_token": n, "ms_per_token": round(ms, 4), "tokens_per_s": round(tok_s, 2),
+            "packed_weight_bytes_per_token": int(packed_bytes), "scale_bytes_per_token": int(scale_bytes),
+            "packed_GBps": round(packed_bytes / (ms / 1e3) / 1e9, 1),
+            "alg_GBps": round((packed_bytes + scale_bytes) / (ms / 1e3) / 1e9, 1),
+            "hbm_roofline_ms_per_token": round((packed_bytes + scale_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+            "launch_floor_ms_per_token": "336 x ~1.5 us (see calibration)"}
 
 
 def main():
@@ -254,6 +406,13 @@ def main():
         "packed_GBps_frac_of_hbm_peak": round(packed_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
         "wall_s_timed_region": round(t_wall, 4),
     }
+    if not args.no_extras:
+        del ws, ss
+        torch.cuda.empty_cache()
+        out["comparison_route"] = [comparison_route(args.config, args.shape), comparison_route(4, 3)]
+        out["decode_sweep"] = decode_sweep()
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads((args.config, args.shape))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -120,6 +120,18 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
                              int64_t N, int64_t K, int32_t group, tern_path path,
                              hipStream_t stream);
 
+/*
+ * tern_dequant -- W[N,K] = t * s, the dense 16-bit weight matrix.
+ * Source: 2kiu.com/news/5082861 §4.1 (the first route: dequantise, then a
+ * library GEMM; the pages measure their kernel against it in §4.3).  This
+ * is the comparison route's first half, not part of tern_matmul.
+ *   packed [N,K/4] uint8, scales [N,K/group] fp16 bits, W [N,K] in w_dtype
+ *   (TERN_F16: exact; TERN_BF16: s rounded to bf16, nearest even).
+ *   group must be 128 and divide K.  packed and W 16-byte aligned.
+ */
+tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W, tern_dtype w_dtype,
+                         int64_t N, int64_t K, int32_t group, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

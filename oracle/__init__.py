@@ -62,6 +62,14 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_round_array.restype = None
     lib.oracle_ulp_array.argtypes = [vp, c_int, i64, vp]
     lib.oracle_ulp_array.restype = None
+    lib.oracle_dequant.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.oracle_dequant.restype = c_int
+    lib.oracle_block_map.argtypes = [vp, i64, i64, i64, vp]
+    lib.oracle_block_map.restype = c_int
+    lib.oracle_quantize_scales.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_quantize_scales.restype = c_int
+    lib.oracle_matmul_s8_cols.argtypes = [vp, c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp]
+    lib.oracle_matmul_s8_cols.restype = c_int
     return lib
 
 
@@ -180,6 +188,64 @@ class Oracle:
                                        _ptr(ms), _ptr(ns), ms.size, _ptr(Y), _ptr(B))
         if rc != 0:
             raise ValueError("oracle_matmul_at: bad arguments")
+        return Y, B
+
+    # --- the comparison route, block map, int8 scales ---------------------
+    def dequant(self, packed: np.ndarray, scale_bits: np.ndarray, N: int, K: int,
+                group: int = 128) -> np.ndarray:
+        """Dense W[N,K] = t * s in float64."""
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+        W = np.empty((N, K), dtype=np.float64)
+        if self.lib.oracle_dequant(_ptr(p), _ptr(s), N, K, group, _ptr(W)) != 0:
+            raise ValueError("oracle_dequant: bad shape")
+        return W
+
+    def block_map(self, packed: np.ndarray, N: int, K: int, group: int = 128) -> np.ndarray:
+        """uint32 [N, ceil(K/group/32)]: bit g%32 of word g/32 set if block g has a nonzero weight."""
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        words = (K // group + 31) // 32
+        out = np.empty((N, words), dtype=np.uint32)
+        if self.lib.oracle_block_map(_ptr(p), N, K, group, _ptr(out)) != 0:
+            raise ValueError("oracle_block_map: bad shape")
+        return out
+
+    def quantize_scales(self, scale_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """(q int8 [N, groups], r float32 [N]) with s ~ q * r (per-row absmax / 127)."""
+        s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+        N, groups = s.shape
+        q = np.empty((N, groups), dtype=np.int8)
+        r = np.empty(N, dtype=np.float32)
+        self.lib.oracle_quantize_scales(_ptr(s), N, groups, _ptr(q), _ptr(r))
+        return q, r
+
+    def matmul_s8(self, x_bits: np.ndarray, x_dtype: str, packed: np.ndarray, q: np.ndarray,
+                  r_f32: np.ndarray, M: int, N: int, K: int, group: int = 128,
+                  threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+        """Y and B with effective scales q[n,g] * r[n] (r given as float32)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        qq = np.ascontiguousarray(q, dtype=np.int8)
+        rb = np.ascontiguousarray(np.asarray(r_f32, dtype=np.float32)).view(np.uint32)
+        Y = np.zeros((M, N), dtype=np.float64)
+        B = np.zeros((M, N), dtype=np.float64)
+        kind = KIND[x_dtype]
+        threads = max(1, min(int(threads), N)) if N > 0 else 1
+        bounds = [N * i // threads for i in range(threads + 1)]
+        errs = []
+
+        def run(a, b):
+            if self.lib.oracle_matmul_s8_cols(_ptr(x), kind, _ptr(p), _ptr(qq), _ptr(rb), M, N, K,
+                                              group, a, b, _ptr(Y), _ptr(B)) != 0:
+                errs.append(1)
+
+        ts = [threading.Thread(target=run, args=(bounds[i], bounds[i + 1])) for i in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        if errs:
+            raise ValueError("oracle_matmul_s8: bad arguments")
         return Y, B
 
     # --- the pass criterion -------------------------------------------------

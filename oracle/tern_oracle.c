@@ -172,6 +172,24 @@ static double x_value(const uint16_t *X, int x_kind, int64_t K, int64_t m, int64
     return x_kind == 1 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
 }
 
+/* The sign-accumulated sum of one block (add for +1, subtract for -1, skip
+ * for 0) of row n against activation row m, and the block's sum of |x|:
+ *   block = sum_{k in [k0,k1), t=+1} x[m,k] - sum_{k in [k0,k1), t=-1} x[m,k] */
+static double block_sum(const uint16_t *X, int x_kind, const uint8_t *packed, int64_t K,
+                        int64_t m, int64_t n, int64_t k0, int64_t k1, double *abs_x) {
+    double block = 0.0, ax = 0.0;
+    for (int64_t k = k0; k < k1; ++k) {
+        double x = x_value(X, x_kind, K, m, k);
+        int t = oracle_weight(packed, K, n, k);
+        if (t == 1) block += x;            /* +1: add      */
+        else if (t == -1) block -= x;      /* -1: subtract */
+                                           /*  0: skip     */
+        ax += fabs(x);
+    }
+    *abs_x = ax;
+    return block;
+}
+
 /* One output element and its error scale:
  *   y = sum_g s[n,g] * (sum_{k in g, t=+1} x[m,k] - sum_{k in g, t=-1} x[m,k])
  *   b = sum_k |x[m,k] * s[n, k/G]|
@@ -183,16 +201,10 @@ static void one_output(const uint16_t *X, int x_kind, const uint8_t *packed,
     double y = 0.0, b = 0.0;
     for (int64_t g = 0; g < groups; ++g) {
         double s = oracle_f16_to_f64(S[n * groups + g]);
-        double block = 0.0;                    /* the block's sign-accumulated sum */
-        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
-            double x = x_value(X, x_kind, K, m, k);
-            int t = oracle_weight(packed, K, n, k);
-            if (t == 1) block += x;            /* +1: add      */
-            else if (t == -1) block -= x;      /* -1: subtract */
-                                               /*  0: skip     */
-            b += fabs(x * s);
-        }
+        double ax;
+        double block = block_sum(X, x_kind, packed, K, m, n, g * G, (g + 1) * G, &ax);
         y += s * block;                        /* scale applied at the block boundary */
+        b += fabs(s) * ax;
     }
     *y_out = y;
     *b_out = b;
@@ -251,4 +263,97 @@ void oracle_round_array(const double *v, int kind, int64_t count, double *out) {
 
 void oracle_ulp_array(const double *v, int kind, int64_t count, double *out) {
     for (int64_t i = 0; i < count; ++i) out[i] = oracle_ulp(v[i], kind);
+}
+
+/* ---------- the dequantised weight matrix (comparison route) ---------- */
+
+/* W[n,k] = t(n,k) * S[n, k/G] in float64 (the dense matrix the pages' first
+ * route multiplies with a library GEMM: 2kiu.com/news/5082861 §4.1). */
+int oracle_dequant(const uint8_t *packed, const uint16_t *S, int64_t N, int64_t K, int64_t G,
+                   double *W) {
+    if (N < 0 || K < 0 || G <= 0 || K % 4 != 0 || K % G != 0) return -1;
+    int64_t groups = K / G;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[n * K + k] = oracle_weight(packed, K, n, k) * oracle_f16_to_f64(S[n * groups + k / G]);
+    return 0;
+}
+
+/* ---------- the all-zero block map ---------- */
+
+/* map[n, g/32] bit (g%32) = 1 when block g of row n holds a nonzero weight
+ * (a code 01 or 10); blocks of only 00 / 11 codes contribute nothing and may
+ * be skipped (2kiu.com/news/5082861 §6: a sparse mask to skip zero blocks).
+ * words_per_row = ceil((K/G) / 32). */
+int oracle_block_map(const uint8_t *packed, int64_t N, int64_t K, int64_t G, uint32_t *map) {
+    if (N < 0 || K < 0 || G <= 0 || K % 4 != 0 || K % G != 0) return -1;
+    int64_t groups = K / G, words = (groups + 31) / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t w = 0; w < words; ++w) map[n * words + w] = 0;
+        for (int64_t g = 0; g < groups; ++g) {
+            int any = 0;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                if (oracle_weight(packed, K, n, k) != 0) any = 1;
+            if (any) map[n * words + g / 32] |= (uint32_t)1 << (g % 32);
+        }
+    }
+    return 0;
+}
+
+/* ---------- int8 scales ---------- */
+
+/* Per-row symmetric int8 quantisation of the fp16 scales (a reading of
+ * 2kiu.com/news/5082861 §6, "compress the FP16 scale further to INT8"):
+ *   r[n]   = fp32( max_g |s[n,g]| / 127 )          (0 when the row's scales are all 0)
+ *   q[n,g] = round-half-even( fp32( s[n,g] / r[n] ) ), within [-127, 127]
+ * The integer is decided in IEEE single precision, the precision the device
+ * kernel divides in, so both sides take the same decision.  The effective
+ * scale is q * r.  r is returned as float32. */
+int oracle_quantize_scales(const uint16_t *S, int64_t N, int64_t groups, int8_t *q, float *r) {
+    if (N < 0 || groups < 0) return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t g = 0; g < groups; ++g) {
+            float a = (float)fabs(oracle_f16_to_f64(S[n * groups + g]));   /* exact: fp16 -> fp32 */
+            if (a > amax) amax = a;
+        }
+        volatile float rn = amax / 127.0f;
+        r[n] = rn;
+        for (int64_t g = 0; g < groups; ++g) {
+            float t = 0.0f;
+            if (rn > 0.0f) {
+                volatile float quot = (float)oracle_f16_to_f64(S[n * groups + g]) / rn;
+                t = nearbyintf(quot);
+            }
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            q[n * groups + g] = (int8_t)t;
+        }
+    }
+    return 0;
+}
+
+/* Y and B as oracle_matmul_cols, with the effective scale q[n,g] * r[n]
+ * (r given as fp32 bits, the stored form). */
+int oracle_matmul_s8_cols(const uint16_t *X, int x_kind, const uint8_t *packed, const int8_t *q,
+                          const uint32_t *r_bits, int64_t M, int64_t N, int64_t K, int64_t G,
+                          int64_t n0, int64_t n1, double *Y, double *B) {
+    if (check_args(M, N, K, G, x_kind)) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1) return -1;
+    int64_t groups = K / G;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = n0; n < n1; ++n) {
+            double rn = oracle_f32_to_f64(r_bits[n]);
+            double y = 0.0, b = 0.0;
+            for (int64_t g = 0; g < groups; ++g) {
+                double s = (double)q[n * groups + g] * rn;
+                double ax;
+                double block = block_sum(X, x_kind, packed, K, m, n, g * G, (g + 1) * G, &ax);
+                y += s * block;
+                b += fabs(s) * ax;
+            }
+            Y[m * N + n] = y;
+            B[m * N + n] = b;
+        }
+    return 0;
 }

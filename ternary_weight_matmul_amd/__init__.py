@@ -23,7 +23,7 @@ from ._lib import (  # noqa: F401
     lib,
     library_path,
 )
-from .ops import matmul, matmul_into, pack, unpack  # noqa: F401
+from .ops import dequant, matmul, matmul_into, pack, shard_columns, shard_k, unpack  # noqa: F401
 
 GROUP = 128
 GEMV_MAX_M = 4

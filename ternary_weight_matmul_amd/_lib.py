@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     L.tern_matmul.restype = c_int
     L.tern_matmul_path.argtypes = [vp, c_int, vp, vp, vp, c_int, i64, i64, i64, i32, c_int, vp]
     L.tern_matmul_path.restype = c_int
+    L.tern_dequant.argtypes = [vp, vp, vp, c_int, i64, i64, i32, vp]
+    L.tern_dequant.restype = c_int
     return L
 
 

@@ -119,4 +119,16 @@ tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed
                             stream);
 }
 
+tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W, tern_dtype w_dtype,
+                         int64_t N, int64_t K, int32_t group, hipStream_t stream) {
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxK || !product_ok(N, K) || K % 4 != 0) return TERN_ERR_SHAPE;
+    if (group <= 0 || K % group != 0) return TERN_ERR_GROUP;
+    if (w_dtype != TERN_F16 && w_dtype != TERN_BF16) return TERN_ERR_DTYPE;
+    if (group != TERN_GROUP) return TERN_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return TERN_OK;
+    if (packed == nullptr || scales == nullptr || W == nullptr) return TERN_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(W, 16) || !aligned(scales, 2)) return TERN_ERR_ALIGN;
+    return from_hip(tern::launch_dequant(packed, scales, W, w_dtype == TERN_BF16 ? 1 : 0, N, K, stream));
+}
+
 }  // extern "C"

@@ -27,6 +27,10 @@ size_t gemv_lds_bytes(int64_t M, int64_t K);
 // Batched path: MFMA GEMM, any M >= 1.
 hipError_t launch_gemm(const GemmArgs &a);
 
+// W[N,K] = t * s in fp16 (w_dtype 0) or bf16 (1).
+hipError_t launch_dequant(const uint8_t *P, const uint16_t *S, void *W, int w_dtype, int64_t N, int64_t K,
+                          hipStream_t stream);
+
 // Y = 0 (K == 0).
 hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
 

@@ -93,3 +93,54 @@ def matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     """Y[M,N] = x[M,K] . (T*S)^T with fp32 accumulation; returns a new tensor."""
     out = torch.empty((x.shape[0], packed.shape[0]), dtype=out_dtype, device=x.device)
     return matmul_into(x, packed, scales, out, group, path)
+
+
+def dequant(packed: torch.Tensor, scales: torch.Tensor, out_dtype: torch.dtype = torch.float16,
+            group: int = 128, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense W[N,K] = t * s (the pages' dequantise-then-GEMM comparison route)."""
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.float16)
+    N = packed.shape[0]
+    K = packed.shape[1] * 4
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=packed.device)
+    if out.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("out must be float16 or bfloat16")
+    _need(out, "out", out.dtype)
+    if tuple(out.shape) != (N, K) or (group > 0 and tuple(scales.shape) != (N, K // group)):
+        raise ValueError("shape mismatch")
+    _check(lib.tern_dequant(packed.data_ptr(), scales.data_ptr(), out.data_ptr(), _TORCH_CODE[out.dtype],
+                            N, K, group, _stream(packed)), "tern_dequant")
+    return out
+
+
+# --- one GPU's share of a sharded layer (no communication here) -------------
+
+def shard_columns(packed: torch.Tensor, scales: torch.Tensor, rank: int, world: int):
+    """Column-parallel shard: whole rows n of W (output columns of Y).
+
+    Rows [rank*N/world, (rank+1)*N/world) of the packed matrix and of the
+    scales (2kiu.com/news/5082861 §5.1: a column split cuts the packed weight
+    and its scale by output rows).  Row slices of row-major tensors are
+    contiguous views: nothing is copied.
+    """
+    N = packed.shape[0]
+    a, b = N * rank // world, N * (rank + 1) // world
+    return packed[a:b], scales[a:b]
+
+
+def shard_k(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, rank: int, world: int,
+            group: int = 128):
+    """Row-parallel shard: a K range cut on 128-weight block boundaries.
+
+    The block boundaries keep every scale with its weights (§3.2, third check,
+    and §5.1 of the same page: a K split must align with the blocks).  Returns
+    contiguous copies of x[:, k0:k1], packed[:, k0/4:k1/4], scales[:, g0:g1];
+    the partial products of all ranks sum to the full result.
+    """
+    K = x.shape[1]
+    groups = K // group
+    g0, g1 = groups * rank // world, groups * (rank + 1) // world
+    k0, k1 = g0 * group, g1 * group
+    return (x[:, k0:k1].contiguous(), packed[:, k0 // 4:k1 // 4].contiguous(),
+            scales[:, g0:g1].contiguous())

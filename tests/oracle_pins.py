@@ -442,4 +442,58 @@ def pin_sampled_matches_full(o):
     assert np.array_equal(Ya, Y[ms, ns]) and np.array_equal(Ba, B[ms, ns])
 
 
+# ---------------------------------------------------------------------------
+# pins: the comparison route, the block map, int8 scales
+# ---------------------------------------------------------------------------
+
+def pin_dequant_dense(o):
+    p = workloads.make_custom(51, 1, 640, 9, reserved_rate=0.05)
+    W = o.dequant(p.packed, p.scales, 9, 640)
+    ref = np_unpack(p.packed).astype(np.float64) * np.repeat(np_decode(p.scales, "f16"), 128, axis=1)
+    assert np.array_equal(W, ref)
+
+
+def pin_block_map(o):
+    rng = workloads.rng_for(102, 0, 0)
+    P = workloads.draw_block_sparse_packed(rng, 7, 128 * 40, 0.5, probs=(0.8, 0.1, 0.1, 0.0))
+    P[3, 5 * 32:6 * 32] = 0xFF          # a block of reserved codes only counts as zero
+    P[4, 7 * 32 + 3] = 0x40             # a single nonzero weight marks its block
+    got = o.block_map(P, 7, 128 * 40)
+    nz = (np_unpack(P).reshape(7, 40, 128) != 0).any(axis=2)
+    want = np.zeros((7, 2), dtype=np.uint32)
+    for n in range(7):
+        for g in range(40):
+            if nz[n, g]:
+                want[n, g // 32] |= np.uint32(1 << (g % 32))
+    assert np.array_equal(got, want)
+    assert not (got[3, 0] >> 5) & 1 and (got[4, 0] >> 7) & 1
+
+
+def pin_quantize_scales(o):
+    p = workloads.make_custom(52, 1, 128 * 24, 30, scale_lo=1e-4, scale_hi=3.0)
+    S = p.scales.copy()
+    S[4] = 0                                            # an all-zero row
+    S[5, 3] = np.float16(-2.5).view(np.uint16)          # a negative scale
+    q, r = o.quantize_scales(S)
+    s32 = S.view(np.float16).astype(np.float32)
+    r_ref = (np.abs(s32).max(axis=1) / np.float32(127)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q_ref = np.where(r_ref[:, None] > 0, np.rint((s32 / r_ref[:, None]).astype(np.float32)), 0)
+    assert np.array_equal(r, r_ref) and np.array_equal(q, q_ref.astype(np.int8))
+    assert np.abs(q).max() == 127 and not q[4].any() and q[5, 3] < 0
+    rel = np.abs(q * r[:, None].astype(np.float64) - s32) / np.maximum(np.abs(s32).max(axis=1, keepdims=True), 1e-30)
+    assert rel.max() <= 0.5 / 127 + 1e-7
+
+
+def pin_matmul_int8_scales(o):
+    p = workloads.make_custom(53, 3, 640, 11, x_dtype="bf16")
+    q, r = o.quantize_scales(p.scales)
+    Y, B = o.matmul_s8(p.x, "bf16", p.packed, q, r, 3, 11, 640, threads=2)
+    S_eff = q.astype(np.float64) * r.astype(np.float64)[:, None]
+    W = np_unpack(p.packed).astype(np.float64) * np.repeat(S_eff, 128, axis=1)
+    X = np_decode(p.x, "bf16")
+    assert np.all(np.abs(Y - X @ W.T) <= 1e-12 * B)
+    assert np.allclose(B, np.abs(X) @ np.abs(np.repeat(S_eff, 128, axis=1)).T, rtol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -40,11 +40,12 @@ MUTANTS = [
     ("row_stride_wrong", "packed[n * (K / 4) + k / 4]", "packed[n * (K / 8) + k / 4]"),
     ("subtract_dropped", "else if (t == -1) block -= x;", "else if (t == -1) block += x;"),
     ("minus_one_skipped", "else if (t == -1) block -= x;", "else if (t == -1) block -= 0.0;"),
-    ("scale_dropped", "y += s * block;", "y += block;"),
-    ("scale_group_zero", "oracle_f16_to_f64(S[n * groups + g])", "oracle_f16_to_f64(S[n * groups])"),
-    ("scale_groups_reversed", "oracle_f16_to_f64(S[n * groups + g])",
-     "oracle_f16_to_f64(S[n * groups + (groups - 1 - g)])"),
-    ("block_last_weight_dropped", "k < (g + 1) * G; ++k", "k < (g + 1) * G - 1; ++k"),
+    ("scale_dropped", "y += s * block;                        /* scale applied", "y += block;                        /* scale applied"),
+    ("scale_group_zero", "double s = oracle_f16_to_f64(S[n * groups + g]);",
+     "double s = oracle_f16_to_f64(S[n * groups]);"),
+    ("scale_groups_reversed", "double s = oracle_f16_to_f64(S[n * groups + g]);",
+     "double s = oracle_f16_to_f64(S[n * groups + (groups - 1 - g)]);"),
+    ("block_last_weight_dropped", "for (int64_t k = k0; k < k1; ++k) {", "for (int64_t k = k0; k < k1 - 1; ++k) {"),
     ("x_reversed_along_k", "uint16_t bits = X[m * K + k];", "uint16_t bits = X[m * K + (K - 1 - k)];"),
     ("x_row_ignored", "uint16_t bits = X[m * K + k];", "uint16_t bits = X[k];"),
     ("f16_bias_off", "ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
@@ -53,13 +54,14 @@ MUTANTS = [
     ("bf16_bias_off", "ldexp((double)(128 + f), e - 134)", "ldexp((double)(128 + f), e - 133)"),
     ("bf16_read_as_f16", "return x_kind == 1 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);",
      "return oracle_f16_to_f64(bits);"),
-    ("bound_signed", "b += fabs(x * s);", "b += x * s;"),
-    ("bound_unscaled", "b += fabs(x * s);", "b += fabs(x);"),
+    ("bound_signed", "        ax += fabs(x);", "        ax += x;"),
+    ("bound_unscaled", "        b += fabs(s) * ax;\n    }\n    *y_out = y;", "        b += ax;\n    }\n    *y_out = y;"),
     ("round_truncates", "nearbyint(a / q) * q", "floor(a / q) * q"),
     ("ulp_too_small", "return ldexp(1.0, e - p + 1);", "return ldexp(1.0, e - p);"),
     ("unpack_row_zero", "T[n * K + k] = (int8_t)oracle_weight(packed, K, n, k);",
      "T[n * K + k] = (int8_t)oracle_weight(packed, K, 0, k);"),
-    ("cols_last_dropped", "for (int64_t n = n0; n < n1; ++n)", "for (int64_t n = n0; n < n1 - 1; ++n)"),
+    ("cols_last_dropped", "for (int64_t n = n0; n < n1; ++n)\n            one_output",
+     "for (int64_t n = n0; n < n1 - 1; ++n)\n            one_output"),
 ]
 
 

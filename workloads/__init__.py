@@ -238,3 +238,29 @@ def draw_block_sparse_packed(rng: np.random.Generator, n: int, k: int, zero_grou
     p = p.reshape(n, k // group, group // 4)
     p[zero] = 0
     return np.ascontiguousarray(p.reshape(n, k // 4))
+
+
+# --- device-side generators (large workloads: the 4.5 GB decode sweep) -------
+
+def draw_packed_device(gen, n: int, k: int, probs=(1 / 3, 1 / 3, 1 / 3, 0.0)):
+    """uint8 [n, k//4] on the generator's device: four independent codes per byte."""
+    import torch
+
+    p = torch.tensor(probs, dtype=torch.float64)
+    cdf = torch.cumsum(p / p.sum(), 0).to(torch.float32).tolist()
+    out = torch.zeros((n, k // 4), dtype=torch.int32, device=gen.device)
+    for i in range(4):
+        u = torch.rand((n, k // 4), generator=gen, device=gen.device)
+        code = (u >= cdf[0]).int() + (u >= cdf[1]).int() + (u >= cdf[2]).int()
+        out += code << (2 * i)
+    return out.to(torch.uint8).contiguous()
+
+
+def draw_scales_device(gen, n: int, groups: int, lo: float, hi: float):
+    """fp16 [n, groups], log-uniform in [lo, hi], on the generator's device."""
+    import math
+
+    import torch
+
+    u = torch.rand((n, groups), generator=gen, device=gen.device, dtype=torch.float64)
+    return torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo))).to(torch.float16).contiguous()
