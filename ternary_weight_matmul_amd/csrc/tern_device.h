@@ -70,6 +70,24 @@ __device__ __forceinline__ void weight_pairs2(uint64_t v, uint32_t &lo, uint32_t
     hi = (uint32_t)(t >> 32) & 0xC000C000u;
 }
 
+// 0xFFFF in each 16-bit half whose bit 15 is set, 0 elsewhere.
+__device__ __forceinline__ uint32_t half_masks(uint32_t u) {
+    typedef short short2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2_t, u) >> (short2_t){15, 15});
+}
+
+// Exact fp16 products t*s for weights (i, i+8) of both words of a transformed
+// pair, s2 = the scale's bits in both halves: s with the code's sign where the
+// field is nonzero, +0 where it is zero (codes 00 and 11).  No arithmetic, so
+// every finite scale gives its exact product.
+template <int I>
+__device__ __forceinline__ void scaled_pairs2(uint64_t v, uint32_t s2, uint32_t &lo, uint32_t &hi) {
+    const uint64_t t = shl64<14 - 2 * I>(v);   // signs at bits 15, 31 (and 47, 63)
+    const uint64_t u = shl64<15 - 2 * I>(v);   // nonzero flags at bits 15, 31 (and 47, 63)
+    lo = (((uint32_t)t & 0x80008000u) ^ s2) & half_masks((uint32_t)u);
+    hi = (((uint32_t)(t >> 32) & 0x80008000u) ^ s2) & half_masks((uint32_t)(u >> 32));
+}
+
 // +-2 / 0 pair for weights (i, i+8) of a transformed word.
 template <int I>
 __device__ __forceinline__ uint32_t weight_pair(uint32_t v) {

@@ -18,9 +18,10 @@
 //     and the global loads run two iterations ahead;
 //   * each lane loads 8 code bytes (32 weights) of its column for each of its
 //     NB column blocks (prefetched two iterations ahead) and decodes them in
-//     registers straight into MFMA B operands: +-2 pairs (tern_device.h);
-//     with fp16 X they are multiplied by the fp16 scale (+-2s, exact); with
-//     bf16 X they stay +-2 and the block's fp32 partial sum is scaled;
+//     registers straight into MFMA B operands: +-2 pairs (tern_device.h),
+//     exact in fp16 and bf16; the block's fp32 partial sum is then scaled by
+//     s/2 in fp32 (the pages' scale-at-the-block-boundary step), so no scale
+//     is ever rounded or overflowed into the 16-bit operand;
 //   * v_mfma_f32_16x16x32_{f16,bf16}: lane l gives A[l%16][8(l/16)+e] and
 //     B[8(l/16)+e][l%16]; the lane's 32 weights of a block are spread over the
 //     4 MFMA k-steps so that the activation fragment of step t is the 16-byte
@@ -55,10 +56,6 @@ __device__ __forceinline__ float4_t mfma16x16x32(const uint4 &a, const uint4 &b,
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                       __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
     }
-}
-
-__device__ __forceinline__ uint32_t mul_pair_f16(uint32_t p, half2_t s2) {
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) * s2);
 }
 
 template <int MB, int NB, int WN, int WK, bool XBF16, int YT>
@@ -169,13 +166,11 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             for (int nb = 0; nb < NB; ++nb)
                 v[nb] = sign_nz_fields64((uint64_t)w0[nb].x | ((uint64_t)w0[nb].y << 32));
 
-            float4_t part[XBF16 ? MB : 1][XBF16 ? NB : 1];
-            if constexpr (XBF16) {
+            float4_t part[MB][NB];
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-            }
+                for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
             const uint8_t *a_base = a_lds + (buf * WK + wk) * A_TILE + li * LDS_ROW + lg * 64;
 
             // k-steps H and H+2 use pairs 4H..4H+3 of word 0 and of word 1:
@@ -190,22 +185,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
                     weight_pairs2<4 * H + 1>(v[nb], lo1, hi1);
                     weight_pairs2<4 * H + 2>(v[nb], lo2, hi2);
                     weight_pairs2<4 * H + 3>(v[nb], lo3, hi3);
-                    uint4 bl = make_uint4(lo0, lo1, lo2, lo3);
-                    uint4 bh = make_uint4(hi0, hi1, hi2, hi3);
-                    if constexpr (!XBF16) {
-                        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)s0[nb]);
-                        const half2_t s2 = {sh, sh};
-                        bl.x = mul_pair_f16(bl.x, s2);
-                        bl.y = mul_pair_f16(bl.y, s2);
-                        bl.z = mul_pair_f16(bl.z, s2);
-                        bl.w = mul_pair_f16(bl.w, s2);
-                        bh.x = mul_pair_f16(bh.x, s2);
-                        bh.y = mul_pair_f16(bh.y, s2);
-                        bh.z = mul_pair_f16(bh.z, s2);
-                        bh.w = mul_pair_f16(bh.w, s2);
-                    }
-                    blo[nb] = bl;
-                    bhi[nb] = bh;
+                    blo[nb] = make_uint4(lo0, lo1, lo2, lo3);
+                    bhi[nb] = make_uint4(hi0, hi1, hi2, hi3);
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
@@ -214,30 +195,24 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
                     const uint4 ah = *reinterpret_cast<const uint4 *>(arow + (H + 2) * 16);   // k-step H+2
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        if constexpr (XBF16) {
-                            part[mb][nb] = mfma16x16x32<true>(al, blo[nb], part[mb][nb]);
-                            part[mb][nb] = mfma16x16x32<true>(ah, bhi[nb], part[mb][nb]);
-                        } else {
-                            acc[mb][nb] = mfma16x16x32<false>(al, blo[nb], acc[mb][nb]);
-                            acc[mb][nb] = mfma16x16x32<false>(ah, bhi[nb], acc[mb][nb]);
-                        }
+                        part[mb][nb] = mfma16x16x32<XBF16>(al, blo[nb], part[mb][nb]);
+                        part[mb][nb] = mfma16x16x32<XBF16>(ah, bhi[nb], part[mb][nb]);
                     }
                 }
             };
             kstep2(std::integral_constant<int, 0>{});
             kstep2(std::integral_constant<int, 1>{});
 
-            if constexpr (XBF16) {           // block boundary: scale the block's sums
+            // block boundary: scale the block's sums (s/2: the operands were +-2)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const float s = f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
+            for (int nb = 0; nb < NB; ++nb) {
+                const float s = f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
-                        acc[mb][nb][1] = fmaf(s, part[mb][nb][1], acc[mb][nb][1]);
-                        acc[mb][nb][2] = fmaf(s, part[mb][nb][2], acc[mb][nb][2]);
-                        acc[mb][nb][3] = fmaf(s, part[mb][nb][3], acc[mb][nb][3]);
-                    }
+                for (int mb = 0; mb < MB; ++mb) {
+                    acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
+                    acc[mb][nb][1] = fmaf(s, part[mb][nb][1], acc[mb][nb][1]);
+                    acc[mb][nb][2] = fmaf(s, part[mb][nb][2], acc[mb][nb][2]);
+                    acc[mb][nb][3] = fmaf(s, part[mb][nb][3], acc[mb][nb][3]);
                 }
             }
         }
@@ -282,7 +257,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     }
 
     // ---- epilogue: lane l holds rows 4(l/16)+i, column l%16 of each 16x16 block ----
-    const float post = XBF16 ? 1.0f : 0.5f;    // the +-2s operand counted each weight twice
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -292,7 +266,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + mb * 16 + lg * 4 + i;
-                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, acc[mb][nb][i] * post);
+                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, acc[mb][nb][i]);
             }
         }
 }
@@ -326,7 +300,12 @@ hipError_t launch_y(const GemmArgs &a) {
 
 }  // namespace
 
+// fp16 X with at least this many rows goes to the 256 x 256 kernel
+// (tern_gemm_big.hip), which shares each weight decode across 256 rows.
+constexpr int64_t kBigMinM = 128;
+
 hipError_t launch_gemm(const GemmArgs &a) {
+    if (a.x_dtype == 0 && a.M >= kBigMinM) return launch_gemm_big(a);
     return a.x_dtype == 1 ? launch_y<true>(a) : launch_y<false>(a);
 }
 

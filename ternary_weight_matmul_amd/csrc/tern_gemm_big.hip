@@ -1,0 +1,266 @@
+// tern_gemm_big.hip -- batched-path kernel for many activation rows (fp16 X).
+//
+// Same product as tern_gemm.hip, Y[M,N] = X[M,K] . (T*S)^T with the weights
+// kept packed in memory and decoded on chip, one fp16 scale per 128-weight
+// block (2kiu.com/news/5082861 §3.1 for the codes, §4.1-§4.3 for decoding in
+// the kernel and reading each scale once per block).  With many activation
+// rows the weight decode can be shared by a large tile, so this kernel is an
+// LDS-staged MFMA GEMM:
+//   * a workgroup of WM x WN waves computes a BM x BN tile of Y, BM = 16 MB WM,
+//     BN = 16 NB WN; wave (wm, wn) owns an (16 MB) x (16 NB) sub-tile (MB x NB
+//     blocks of 16 x 16, fp32 accumulators);
+//   * per 64-wide K step both operands are staged in LDS in natural k order:
+//     X[BM rows, 64] as read, and W[BN columns, 64] decoded once per
+//     workgroup into exact fp16 products t*s (the scale with the code's sign
+//     where the code is nonzero, +0 elsewhere) -- exact for every finite
+//     scale, so the MFMA sums the pages' products directly;
+//   * LDS rows are 128 bytes with their eight 16-byte chunks XOR-swizzled by
+//     (row / 2) mod 8: the 16 lanes reading one MFMA fragment, and the lanes
+//     writing a row, touch 64 distinct banks;
+//   * both tiles are double-buffered, one barrier per step; an iteration
+//     writes step s+1 (held in registers) to LDS, issues the global loads of
+//     step s+2 and runs the MFMAs of step s, with no branches, so the decode
+//     can interleave with the MFMAs and each load has a step to land; each
+//     group of 8 lanes reads one 128-byte row segment of X (coalesced);
+//   * v_mfma_f32_16x16x32_f16: lane l supplies A[l%16][8(l/16)+e] and
+//     B[8(l/16)+e][l%16], e = 0..7: one 16-byte chunk of an LDS row.
+// Workgroups are renumbered so that each XCD gets a contiguous run of tiles
+// (tile_n fastest): workgroups resident on one XCD share activation rows in
+// its L2.
+#include <hip/hip_runtime.h>
+
+#include "tern_device.h"
+#include "tern_kernels.h"
+
+namespace tern {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int KS = 64;       // K per step
+constexpr int ROWB = 128;    // bytes per LDS row (KS fp16)
+
+// byte offset of 16-byte chunk c of row r inside a tile
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <int WM, int WN, int MB, int NB, int YT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *__restrict__ X,
+                                                                 const uint8_t *__restrict__ P,
+                                                                 const uint16_t *__restrict__ S,
+                                                                 void *__restrict__ Y, int M, int N, int K,
+                                                                 int tiles_m, int tiles_n) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int BM = 16 * MB * WM;
+    constexpr int BN = 16 * NB * WN;
+    constexpr int A_TILE = BM * ROWB;
+    constexpr int W_TILE = BN * ROWB;
+    constexpr int AP = BM * 8 / NT;          // 16-byte X chunks per thread per step
+    constexpr int RSTEP = NT / 8;            // rows between a thread's chunks
+    static_assert(AP * NT == BM * 8 && AP == 4, "four X chunks per thread (kept in scalars)");
+    static_assert(RSTEP % 16 == 0, "swizzle must not depend on the chunk index");
+    static_assert(2 * BN <= NT, "one thread per 32 decoded weights");
+    // [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * A_TILE + 2 * W_TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave - wm * WN;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
+    const int tile_m = tile / tiles_n;
+    const int tile_n = tile - tile_m * tiles_n;
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+    const int64_t row_bytes = K >> 2;
+    const int groups = K >> 7;
+    const int nsteps = K / KS;      // >= 2: K is a positive multiple of 128
+
+    // X loader: chunk j of this thread is row RSTEP j + tid/8, chunk tid%8 of the step;
+    // rows past M are clamped to M-1 (read, never stored)
+    const int xr = tid >> 3;
+    const int xc = tid & 7;
+    const uint16_t *x_src0 = X + (int64_t)min(m0 + xr, M - 1) * K + xc * 8;
+    const uint16_t *x_src1 = X + (int64_t)min(m0 + RSTEP + xr, M - 1) * K + xc * 8;
+    const uint16_t *x_src2 = X + (int64_t)min(m0 + 2 * RSTEP + xr, M - 1) * K + xc * 8;
+    const uint16_t *x_src3 = X + (int64_t)min(m0 + 3 * RSTEP + xr, M - 1) * K + xc * 8;
+    const int x_dst = swz(xr, xc);    // + RSTEP*ROWB j (same swizzle)
+
+    // W loader: thread t < 2 BN decodes column t/2, weights 32 h .. 32 h + 31 of the step
+    const bool w_role = (2 * BN == NT) || tid < 2 * BN;
+    const int wc_col = (tid >> 1) % BN;
+    const int wc_h = tid & 1;
+    const int64_t wn_g = min(n0 + wc_col, N - 1);                           // clamped: never stored
+    const uint8_t *w_src = P + wn_g * row_bytes + 8 * wc_h;
+    const uint16_t *s_src = S + wn_g * groups;
+    const int w_dst0 = swz(wc_col, 4 * wc_h + 0);
+    const int w_dst1 = swz(wc_col, 4 * wc_h + 1);
+    const int w_dst2 = swz(wc_col, 4 * wc_h + 2);
+    const int w_dst3 = swz(wc_col, 4 * wc_h + 3);
+
+    uint4 xa0, xa1, xa2, xa3;
+    uint2 wcode;
+    uint32_t sbits;
+    auto load = [&](int s) {
+        const int64_t o = (int64_t)s * KS;
+        xa0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
+        xa1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
+        xa2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
+        xa3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
+        wcode = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
+        sbits = s_src[s >> 1];
+    };
+    auto store_x = [&](int buf) {
+        uint8_t *a_t = lds + buf * A_TILE + x_dst;
+        *reinterpret_cast<uint4 *>(a_t) = xa0;
+        *reinterpret_cast<uint4 *>(a_t + RSTEP * ROWB) = xa1;
+        *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = xa2;
+        *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = xa3;
+    };
+    auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
+        if (w_role) {
+            const uint64_t v = sign_nz_fields64((uint64_t)wc.x | ((uint64_t)wc.y << 32));
+            const uint32_t s2 = sb | (sb << 16);
+            // products of weights (i, i+8) of code word 0 (a*) and word 1 (b*)
+            uint32_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
+            scaled_pairs2<0>(v, s2, a0, b0);
+            scaled_pairs2<1>(v, s2, a1, b1);
+            scaled_pairs2<2>(v, s2, a2, b2);
+            scaled_pairs2<3>(v, s2, a3, b3);
+            scaled_pairs2<4>(v, s2, a4, b4);
+            scaled_pairs2<5>(v, s2, a5, b5);
+            scaled_pairs2<6>(v, s2, a6, b6);
+            scaled_pairs2<7>(v, s2, a7, b7);
+            uint8_t *w_t = lds + 2 * A_TILE + buf * W_TILE;
+            // natural order: chunk 4h = weights 0..7 of word 0, 4h+1 = 8..15, 4h+2/3 from word 1
+            *reinterpret_cast<uint4 *>(w_t + w_dst0) =
+                make_uint4(pair_lo(a0, a1), pair_lo(a2, a3), pair_lo(a4, a5), pair_lo(a6, a7));
+            *reinterpret_cast<uint4 *>(w_t + w_dst1) =
+                make_uint4(pair_hi(a0, a1), pair_hi(a2, a3), pair_hi(a4, a5), pair_hi(a6, a7));
+            *reinterpret_cast<uint4 *>(w_t + w_dst2) =
+                make_uint4(pair_lo(b0, b1), pair_lo(b2, b3), pair_lo(b4, b5), pair_lo(b6, b7));
+            *reinterpret_cast<uint4 *>(w_t + w_dst3) =
+                make_uint4(pair_hi(b0, b1), pair_hi(b2, b3), pair_hi(b4, b5), pair_hi(b6, b7));
+        }
+    };
+
+    float4_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // fragment offsets: row li of a 16-row block, chunk 4t + lg; the swizzle
+    // term depends on li only because every block starts at a multiple of 16
+    const int a_off = (16 * MB * wm + li) * ROWB;
+    const int b_off = 2 * A_TILE + (16 * NB * wn + li) * ROWB;
+    const int f0 = ((0 + lg) ^ (li >> 1)) << 4;
+    const int f1 = ((4 + lg) ^ (li >> 1)) << 4;
+    // one half of a step (32 of its 64 k): fragment reads, then MB x NB MFMAs
+    half8_t af[MB], bf[NB];
+    auto read_frags = [&](int buf, int f) {
+        const uint8_t *a_t = lds + buf * A_TILE + a_off + f;
+        const uint8_t *b_t = lds + buf * W_TILE + b_off + f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bf[nb] = *reinterpret_cast<const half8_t *>(b_t + nb * 16 * ROWB);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const half8_t *>(a_t + mb * 16 * ROWB);
+    };
+    auto mfmas = [&]() {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    };
+
+    load(0);
+    store_x(0);
+    store_w(0, wcode, sbits);
+    load(1);
+    __syncthreads();
+    // steps 0 .. nsteps-2: write step s+1 (loaded one iteration earlier) to
+    // the other buffer, issue the loads of step s+2 (the last ones repeat step
+    // nsteps-1: in bounds, unused), then decode step s+1's weights while the
+    // MFMAs of step s run: decode instructions are spread between the MFMAs
+    for (int s = 0; s < nsteps - 1; ++s) {
+        const int buf = s & 1;
+        store_x(buf ^ 1);
+        const uint2 wc = wcode;
+        const uint32_t sb = sbits;
+        load(min(s + 2, nsteps - 1));
+        // first half's fragments are read before the decode writes to LDS, so
+        // its MFMAs do not wait for them
+        read_frags(buf, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        store_w(buf ^ 1, wc, sb);
+        mfmas();
+        read_frags(buf, f1);
+        mfmas();
+        __syncthreads();
+    }
+    read_frags((nsteps - 1) & 1, f0);
+    mfmas();
+    read_frags((nsteps - 1) & 1, f1);
+    mfmas();
+
+    // epilogue: lane l holds rows 4(l/16)+i, column l%16 of each 16 x 16 block
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = n0 + 16 * NB * wn + 16 * nb + li;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + 16 * MB * wm + 16 * mb + 4 * lg + i;
+                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, acc[mb][nb][i]);
+            }
+        }
+}
+
+template <int WM, int WN, int MB, int NB>
+struct Tile {
+    static constexpr int BM = 16 * MB * WM, BN = 16 * NB * WN;
+    static int64_t count(const GemmArgs &a) { return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
+    template <int YT>
+    static hipError_t launch(const GemmArgs &a) {
+        const int64_t tiles_n = (a.N + BN - 1) / BN;
+        const int64_t tiles_m = (a.M + BM - 1) / BM;
+        if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, YT>), dim3((unsigned)(tiles_n * tiles_m)),
+                           dim3(64 * WM * WN), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y,
+                           (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
+        return hipGetLastError();
+    }
+};
+
+using Tile256 = Tile<2, 4, 8, 4>;   // 256 x 256, 8 waves of 128 x 64
+using Tile64 = Tile<2, 2, 4, 2>;    // 128 x 64, 4 waves of 64 x 32 (several workgroups per CU)
+
+template <int YT>
+hipError_t launch_big_y(const GemmArgs &a) {
+    // 256 x 256 tiles run one workgroup per CU: take them while they still
+    // cover three quarters of the 256 CUs, otherwise the small tiles
+    if (Tile256::count(a) >= 192) return Tile256::launch<YT>(a);
+    return Tile64::launch<YT>(a);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_big(const GemmArgs &a) {
+    switch (a.y_dtype) {
+    case 0: return launch_big_y<0>(a);
+    case 1: return launch_big_y<1>(a);
+    default: return launch_big_y<2>(a);
+    }
+}
+
+}  // namespace tern

@@ -26,6 +26,9 @@ size_t gemv_lds_bytes(int64_t M, int64_t K);
 
 // Batched path: MFMA GEMM, any M >= 1.
 hipError_t launch_gemm(const GemmArgs &a);
+// Batched path for many rows with fp16 X: 256 x 256 tiles, weights decoded
+// once per workgroup into LDS.
+hipError_t launch_gemm_big(const GemmArgs &a);
 
 // W[N,K] = t * s in fp16 (w_dtype 0) or bf16 (1).
 hipError_t launch_dequant(const uint8_t *P, const uint16_t *S, void *W, int w_dtype, int64_t N, int64_t K,

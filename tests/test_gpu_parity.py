@@ -147,11 +147,26 @@ def test_outliers_and_wide_scales():
         _full(q, path)
 
 
+@pytest.mark.parametrize("M,path", [(1, "gemv"), (3, "gemv"), (8, "mfma"), (40, "mfma"), (200, "mfma"),
+                                    (300, "auto")])
+@pytest.mark.parametrize("xd", ["f16", "bf16"])
+def test_scales_near_fp16_max_and_negative(M, path, xd):
+    """Scales up to the largest fp16 (65504), half of them negative.
+
+    t*s is finite for every finite fp16 scale, so no kernel may form an
+    operand that overflows (2*s does, for |s| > 32752)."""
+    p = workloads.make_custom(900 + M, M, 1024, 96, x_dtype=xd, y_dtype="f32",
+                              scale_lo=8192.0, scale_hi=65504.0, x_sigma=1e-3)
+    p.scales = p.scales ^ np.where(np.arange(p.scales.size).reshape(p.scales.shape) % 2 == 1,
+                                   np.uint16(0x8000), np.uint16(0))
+    _full(p, path)
+
+
 # ---------------------------------------------------------------------------
 # exact arithmetic: bit-exact against the oracle rounded to the output type
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16)])
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16), (200, 1024, 80)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
 @pytest.mark.parametrize("yd", ["f32", "bf16", "f16"])
 def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
@@ -171,6 +186,28 @@ def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
         y = tern.matmul(x, w, s, out_dtype=TORCH_DT[yd], path=path)
         got = O().decode(out_bits(y, yd), yd)
         assert np.array_equal(got, want), (path, np.argwhere(got != want)[:5])
+
+
+@pytest.mark.parametrize("M,K,N,yd", [(2000, 256, 6000, "f16"), (1999, 384, 6001, "f32")])
+def test_large_tiles_ragged(M, K, N, yd):
+    """Shapes that take the 256 x 256 tiles (at least 192 of them) with
+    ragged row and column tails, compared element by element."""
+    p = workloads.make_custom(M + N, M, K, N, x_dtype="f16", y_dtype=yd, reserved_rate=0.02)
+    _full(p, "auto")
+
+
+def test_large_tiles_exact_bit_exact():
+    """Exact arithmetic on the 256 x 256 tiles: bit-identical to the oracle."""
+    M, K, N = 2000, 256, 6000
+    rng = np.random.default_rng(4242)
+    xbits = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
+    P = O().pack(workloads.draw_ternary(77, N, K))
+    sbits = (2.0 ** rng.integers(-4, 1, (N, K // 128))).astype(np.float16).view(np.uint16)
+    Y, _ = O().matmul(xbits, "f16", P, sbits, M, N, K, threads=8)
+    y = tern.matmul(bits_to_device(xbits, "f16"), torch.from_numpy(P).to(device()),
+                    bits_to_device(sbits, "f16"), out_dtype=torch.float32)
+    got = O().decode(out_bits(y, "f32"), "f32")
+    assert np.array_equal(got, O().round(Y, "f32"))
 
 
 # ---------------------------------------------------------------------------
