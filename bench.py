@@ -257,6 +257,35 @@ def comparison_route(cid, si):
             "note": "weights resident (no rotation) for both routes"}
 
 
+def int8_scale_variant():
+    """fp16 block scales vs int8 codes with a per-row fp32 factor (tern_matmul_s8) on the
+    decode and batched shapes, same protocol (weights rotated over 1 GB)."""
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    res = []
+    for cid, si in ((2, 0), (3, 0), (3, 1), (3, 4), (4, 0)):
+        p = workloads.make_problem(cid, si)
+        sh = p.shape
+        x, ws, ss, y, copies, _ = _device_problem(p, 1.0)
+        qr = [tern.quantize_scales(s) for s in ss]
+        steps = 100 if sh.M > 16 else 500
+        t16 = _graph_time_ms(lambda i: tern.matmul_into(x, ws[i % copies], ss[i % copies], y), steps, 10)
+        t8 = _graph_time_ms(lambda i: tern.matmul_s8_into(x, ws[i % copies], qr[i % copies][0],
+                                                          qr[i % copies][1], y), steps, 10)
+        packed = sh.N * sh.K // 4
+        res.append({"workload": f"{workloads.CONFIGS[cid].name} M={sh.M} K={sh.K} N={sh.N}",
+                    "fp16_scales_us": round(t16 * 1e3, 3), "int8_scales_us": round(t8 * 1e3, 3),
+                    "int8_over_fp16": round(t8 / t16, 4),
+                    "weight_bytes_fp16_scales": int(packed + sh.N * (sh.K // 128) * 2),
+                    "weight_bytes_int8_scales": int(packed + sh.N * (sh.K // 128) + 4 * sh.N)})
+        del x, ws, ss, y, qr
+        torch.cuda.empty_cache()
+    return res
+
+
 def decode_sweep(reps: int = 3):
     """One token through 48 layers x 7 projections at M=1 (q, k, v, o 5120->5120; gate, up
     5120->17408; down 17408->5120): 336 launches over distinct weights captured in one graph."""
@@ -412,6 +441,7 @@ def main():
         out["comparison_route"] = [comparison_route(args.config, args.shape), comparison_route(4, 3)]
         out["decode_sweep"] = decode_sweep()
         torch.cuda.empty_cache()
+        out["int8_scales"] = int8_scale_variant()
         out["other_workloads"] = other_workloads((args.config, args.shape))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)

@@ -101,8 +101,7 @@ tern_status tern_unpack(const uint8_t *packed, int8_t *T, int64_t N, int64_t K, 
  *                       to nearest-even into bf16/fp16, overflow gives inf
  *   group    must be 128 (TERN_ERR_UNSUPPORTED otherwise) and divide K
  * Result accuracy: |Y - exact| <= 2e-3 * sum_k |X[m,k] * S[n,k/128]| + one
- * ulp of y_dtype, for finite inputs.  The batched (MFMA) path with fp16 X
- * forms 2*S in fp16, so it needs |S| < 32768 there.
+ * ulp of y_dtype, for finite inputs (every finite fp16 scale).
  */
 tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
                         const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,
@@ -131,6 +130,37 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
  */
 tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W, tern_dtype w_dtype,
                          int64_t N, int64_t K, int32_t group, hipStream_t stream);
+
+/*
+ * tern_quantize_scales -- int8 scale codes for tern_matmul_s8.
+ * Source: 2kiu.com/news/5082861 §6 (next steps: compress the fp16 block
+ * scale further to INT8).  The pages do not fix the scheme; this library's
+ * reading is a symmetric code per output row with one fp32 factor:
+ *   row_factor[n]  = max_g |S[n,g]| / 127            (fp32 division)
+ *   scales_q[n,g]  = round-to-nearest-even(S[n,g] / row_factor[n]),
+ *                    clamped to [-127, 127]; 0 for a row whose scales are 0
+ * so the effective scale is scales_q[n,g] * row_factor[n] (relative error
+ * up to 1/254 of the row's largest scale).  Both divisions are IEEE fp32.
+ *   scales [N,K/group] fp16 bits (2-byte aligned), scales_q [N,K/group]
+ *   int8, row_factor [N] fp32 (4-byte aligned).  group must be 128.
+ */
+tern_status tern_quantize_scales(const uint16_t *scales, int8_t *scales_q, float *row_factor, int64_t N,
+                                 int64_t K, int32_t group, hipStream_t stream);
+
+/*
+ * tern_matmul_s8 -- tern_matmul_path with int8 block scales:
+ *   Y[m,n] = sum_g (scales_q[n,g] * row_factor[n]) * sum_{k in g} t[n,k] X[m,k]
+ * Source: 2kiu.com/news/5082861 §6 (INT8 scales, halving the scale traffic:
+ * 1 byte per 128 weights instead of 2), with §4.2 for everything else.
+ * Arguments, layouts, paths and errors as tern_matmul_path, with the fp16
+ * scales replaced by scales_q [N,K/128] int8 and row_factor [N] fp32
+ * (4-byte aligned; NULL only when M, N or K is 0).  The MFMA path runs the
+ * 64 x 256 / 16 x 64 kernels for every M.  Accuracy: the tern_matmul bound
+ * with S[n,g] = scales_q[n,g] * row_factor[n].
+ */
+tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *packed_W, const int8_t *scales_q,
+                           const float *row_factor, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,
+                           int64_t K, int32_t group, tern_path path, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,10 @@ def _load() -> ctypes.CDLL:
     L.tern_matmul_path.restype = c_int
     L.tern_dequant.argtypes = [vp, vp, vp, c_int, i64, i64, i32, vp]
     L.tern_dequant.restype = c_int
+    L.tern_quantize_scales.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.tern_quantize_scales.restype = c_int
+    L.tern_matmul_s8.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, i64, i64, i64, i32, c_int, vp]
+    L.tern_matmul_s8.restype = c_int
     return L
 
 

@@ -28,8 +28,9 @@ tern_status check_pack_args(const void *T, const void *P, int64_t N, int64_t K) 
 
 size_t dtype_size(tern_dtype d) { return d == TERN_F32 ? 4 : 2; }
 
-tern_status check_matmul_args(const void *X, tern_dtype x_dtype, const uint8_t *W, const uint16_t *S,
-                              void *Y, tern_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+// S is the scale array (fp16 values, or int8 codes with s_align 1)
+tern_status check_matmul_args(const void *X, tern_dtype x_dtype, const uint8_t *W, const void *S,
+                              uintptr_t s_align, void *Y, tern_dtype y_dtype, int64_t M, int64_t N, int64_t K,
                               int32_t group) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxK) return TERN_ERR_SHAPE;
     if (!product_ok(M, N) || !product_ok(M, K) || !product_ok(N, K)) return TERN_ERR_SHAPE;
@@ -43,7 +44,7 @@ tern_status check_matmul_args(const void *X, tern_dtype x_dtype, const uint8_t *
     if (!aligned(Y, dtype_size(y_dtype))) return TERN_ERR_ALIGN;
     if (K == 0) return TERN_OK;
     if (X == nullptr || W == nullptr || S == nullptr) return TERN_ERR_NULL;
-    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(S, 2)) return TERN_ERR_ALIGN;
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(S, s_align)) return TERN_ERR_ALIGN;
     return TERN_OK;
 }
 
@@ -89,7 +90,7 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
                              const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M,
                              int64_t N, int64_t K, int32_t group, tern_path path,
                              hipStream_t stream) {
-    const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group);
+    const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales, 2, Y, y_dtype, M, N, K, group);
     if (st != TERN_OK) return st;
     if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA)
         return TERN_ERR_UNSUPPORTED;
@@ -102,6 +103,8 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
     a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
     a.W = packed_W;
     a.S = scales;
+    a.Q = nullptr;
+    a.R = nullptr;
     a.Y = Y;
     a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
     a.M = M;
@@ -117,6 +120,48 @@ tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed
                         hipStream_t stream) {
     return tern_matmul_path(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group, TERN_PATH_AUTO,
                             stream);
+}
+
+tern_status tern_quantize_scales(const uint16_t *scales, int8_t *scales_q, float *row_factor, int64_t N,
+                                 int64_t K, int32_t group, hipStream_t stream) {
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxK || !product_ok(N, K) || K % 4 != 0) return TERN_ERR_SHAPE;
+    if (group <= 0 || K % group != 0) return TERN_ERR_GROUP;
+    if (group != TERN_GROUP) return TERN_ERR_UNSUPPORTED;
+    if (N == 0) return TERN_OK;
+    if (row_factor == nullptr) return TERN_ERR_NULL;
+    if (K > 0 && (scales == nullptr || scales_q == nullptr)) return TERN_ERR_NULL;
+    if (!aligned(scales, 2) || !aligned(row_factor, 4)) return TERN_ERR_ALIGN;
+    return from_hip(tern::launch_quantize_scales(scales, scales_q, row_factor, N, K / group, stream));
+}
+
+tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *packed_W, const int8_t *scales_q,
+                           const float *row_factor, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,
+                           int64_t K, int32_t group, tern_path path, hipStream_t stream) {
+    const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales_q, 1, Y, y_dtype, M, N, K, group);
+    if (st != TERN_OK) return st;
+    if (M > 0 && N > 0 && K > 0 && row_factor == nullptr) return TERN_ERR_NULL;
+    if (!aligned(row_factor, 4)) return TERN_ERR_ALIGN;
+    if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA)
+        return TERN_ERR_UNSUPPORTED;
+    if (path == TERN_PATH_GEMV && M > 0 && K > 0 && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return TERN_OK;
+    if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
+
+    tern::GemmArgs a;
+    a.X = X;
+    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
+    a.W = packed_W;
+    a.S = nullptr;
+    a.Q = scales_q;
+    a.R = row_factor;
+    a.Y = Y;
+    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.stream = stream;
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && gemv_fits(M, K));
+    return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 
 tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W, tern_dtype w_dtype,

@@ -58,10 +58,13 @@ __device__ __forceinline__ float4_t mfma16x16x32(const uint4 &a, const uint4 &b,
     }
 }
 
-template <int MB, int NB, int WN, int WK, bool XBF16, int YT>
+// S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N].
+template <int MB, int NB, int WN, int WK, bool XBF16, int YT, bool S8>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ X,
                                                              const uint8_t *__restrict__ P,
                                                              const uint16_t *__restrict__ S,
+                                                             const int8_t *__restrict__ Q,
+                                                             const float *__restrict__ R,
                                                              void *__restrict__ Y, int M, int N, int K,
                                                              int tiles_m, int tiles_n) {
     constexpr int BM = 16 * MB;
@@ -136,7 +139,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         for (int nb = 0; nb < NB; ++nb) {
             const int64_t n = min(n0 + nb * 16 + li, N - 1);
             w[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
-            s[nb] = S[n * groups + kb];
+            if constexpr (S8) s[nb] = (uint32_t)(int32_t)Q[n * groups + kb];
+            else s[nb] = S[n * groups + kb];
         }
     };
 
@@ -147,7 +151,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     uint2 w0[NB], w1[NB];
-    uint32_t s0[NB], s1[NB];
+    uint32_t s0[NB], s1[NB];    // fp16 scale bits, or the sign-extended int8 code
+    float rowf[NB];             // S8: half the row factor of this lane's column
+    if constexpr (S8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) rowf[nb] = R[min(n0 + nb * 16 + li, N - 1)] * 0.5f;
+    }
     load_a(0);
     load_w(0, w0, s0);
     store_a(0);
@@ -206,7 +215,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             // block boundary: scale the block's sums (s/2: the operands were +-2)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float s = f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
+                const float s = S8 ? (float)(int32_t)s0[nb] * rowf[nb]
+                                   : f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
@@ -271,42 +281,45 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         }
 }
 
-template <int MB, int NB, int WN, int WK, bool XBF16, int YT>
+template <int MB, int NB, int WN, int WK, bool XBF16, int YT, bool S8>
 hipError_t launch_t(const GemmArgs &a) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
     const int64_t tiles_m = (a.M + BM - 1) / BM;
     if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XBF16, YT>), dim3((unsigned)(tiles_n * tiles_m)),
-                       dim3(64 * WN * WK), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y,
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XBF16, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
+                       dim3(64 * WN * WK), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
                        (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
-template <bool XBF16, int YT>
+template <bool XBF16, int YT, bool S8>
 hipError_t launch_shape(const GemmArgs &a) {
-    if (a.M <= 16) return launch_t<1, 2, 2, 4, XBF16, YT>(a);        // 16 x 64 tiles, K split over 4 waves
-    else return launch_t<4, 4, 4, 1, XBF16, YT>(a);                  // 64 x 256
+    if (a.M <= 16) return launch_t<1, 2, 2, 4, XBF16, YT, S8>(a);        // 16 x 64 tiles, K split over 4 waves
+    else return launch_t<4, 4, 4, 1, XBF16, YT, S8>(a);                  // 64 x 256
 }
 
-template <bool XBF16>
+template <bool XBF16, bool S8>
 hipError_t launch_y(const GemmArgs &a) {
     switch (a.y_dtype) {
-    case 0: return launch_shape<XBF16, 0>(a);
-    case 1: return launch_shape<XBF16, 1>(a);
-    default: return launch_shape<XBF16, 2>(a);
+    case 0: return launch_shape<XBF16, 0, S8>(a);
+    case 1: return launch_shape<XBF16, 1, S8>(a);
+    default: return launch_shape<XBF16, 2, S8>(a);
     }
 }
 
 }  // namespace
 
-// fp16 X with at least this many rows goes to the 256 x 256 kernel
-// (tern_gemm_big.hip), which shares each weight decode across 256 rows.
+// fp16 X and fp16 scales with at least this many rows go to the LDS-staged
+// kernel of tern_gemm_big.hip, which shares each weight decode across the
+// rows of a large tile (its exact t*s operand needs an fp16 scale, so int8
+// scales stay here).
 constexpr int64_t kBigMinM = 128;
 
 hipError_t launch_gemm(const GemmArgs &a) {
+    if (a.Q != nullptr) return a.x_dtype == 1 ? launch_y<true, true>(a) : launch_y<false, true>(a);
     if (a.x_dtype == 0 && a.M >= kBigMinM) return launch_gemm_big(a);
-    return a.x_dtype == 1 ? launch_y<true>(a) : launch_y<false>(a);
+    return a.x_dtype == 1 ? launch_y<true, false>(a) : launch_y<false, false>(a);
 }
 
 }  // namespace tern

@@ -69,10 +69,14 @@ __device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M
     step(std::integral_constant<int, 7>{});
 }
 
-template <int M, bool XBF16, int YT, int SPW>
+// S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N]
+// (the int8-scale variant) instead of fp16 values S[N,K/128].
+template <int M, bool XBF16, int YT, int SPW, bool S8>
 __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
+                                                     const int8_t *__restrict__ Q,
+                                                     const float *__restrict__ R,
                                                      void *__restrict__ Y, int N, int K) {
     extern __shared__ uint4 lds[];
     const int nsteps = (K + STEP - 1) / STEP;
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
         }
     }
     uint4 code[SPW][4];
-    uint32_t sbits[SPW][4];
+    uint32_t sbits[SPW][4];     // fp16 scale bits, or the sign-extended int8 code
+    float rowf[4];              // S8: the row factor of rows n0 + 4j + r
 #pragma unroll
     for (int si = 0; si < SPW; ++si) {
         const int c = min((s_begin + si) * 16 + kk, nchunks - 1);
@@ -118,8 +123,13 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
         for (int j = 0; j < 4; ++j) {
             const int64_t n = min(n0 + 4 * j + r, N - 1);
             code[si][j] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
-            sbits[si][j] = S[n * groups + (c >> 1)];
+            if constexpr (S8) sbits[si][j] = (uint32_t)(int32_t)Q[n * groups + (c >> 1)];
+            else sbits[si][j] = S[n * groups + (c >> 1)];
         }
+    }
+    if constexpr (S8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rowf[j] = R[min(n0 + 4 * j + r, N - 1)] * 0.5f;
     }
 
     // ---- 2. stage this wave's activations, pair-interleaved ----
@@ -170,7 +180,8 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
 #pragma unroll
                 for (int m = 0; m < MC; ++m) part[m] = 0.f;
                 chunk_dot<MC, XBF16>(code[si][j], xq, part);
-                const float s = f16_bits_to_float((uint16_t)sbits[si][j]) * 0.5f;
+                const float s = S8 ? (float)(int32_t)sbits[si][j] * rowf[j]
+                                   : f16_bits_to_float((uint16_t)sbits[si][j]) * 0.5f;
 #pragma unroll
                 for (int m = 0; m < MC; ++m)
                     acc[j][mb + m] = kact ? fmaf(s, part[m], acc[j][mb + m]) : acc[j][mb + m];
@@ -220,9 +231,9 @@ GemvShape gemv_shape(int64_t M, int64_t K) {
     return g;
 }
 
-template <int M, bool XBF16, int YT, int SPW>
+template <int M, bool XBF16, int YT, int SPW, bool S8>
 hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
-    auto kern = gemv_kernel<M, XBF16, YT, SPW>;
+    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8>;
     if (g.lds > 64 * 1024) {
         // raise the dynamic-LDS limit once per device (not a stream operation,
         // so it is kept out of any graph capture after the first call)
@@ -241,33 +252,39 @@ hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
     const dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
     const dim3 block((unsigned)(64 * g.nwaves));
     hipLaunchKernelGGL(kern, grid, block, g.lds, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S,
-                       a.Y, (int)a.N, (int)a.K);
+                       a.Q, a.R, a.Y, (int)a.N, (int)a.K);
     return hipGetLastError();
 }
 
-template <int M, bool XBF16, int YT>
+template <int M, bool XBF16, int YT, bool S8>
 hipError_t launch_gemv_s(const GemmArgs &a) {
     const GemvShape g = gemv_shape(M, a.K);
-    switch (g.spw) {
-    case 1: return launch_gemv_t<M, XBF16, YT, 1>(a, g);
-    case 2: return launch_gemv_t<M, XBF16, YT, 2>(a, g);
-    case 3: return launch_gemv_t<M, XBF16, YT, 3>(a, g);
-    default: return launch_gemv_t<M, XBF16, YT, 4>(a, g);
+    if constexpr (M == 1) {   // gemv_lds_bytes admits at most two steps per wave for M = 1
+        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
+        return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
+    } else {
+        switch (g.spw) {
+        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
+        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
+        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8>(a, g);
+        default: return launch_gemv_t<M, XBF16, YT, 4, S8>(a, g);
+        }
     }
 }
 
-template <int M, bool XBF16>
+template <int M, bool XBF16, bool S8>
 hipError_t launch_gemv_y(const GemmArgs &a) {
     switch (a.y_dtype) {
-    case 0: return launch_gemv_s<M, XBF16, 0>(a);
-    case 1: return launch_gemv_s<M, XBF16, 1>(a);
-    default: return launch_gemv_s<M, XBF16, 2>(a);
+    case 0: return launch_gemv_s<M, XBF16, 0, S8>(a);
+    case 1: return launch_gemv_s<M, XBF16, 1, S8>(a);
+    default: return launch_gemv_s<M, XBF16, 2, S8>(a);
     }
 }
 
 template <int M>
 hipError_t launch_gemv_m(const GemmArgs &a) {
-    return a.x_dtype == 1 ? launch_gemv_y<M, true>(a) : launch_gemv_y<M, false>(a);
+    if (a.Q != nullptr) return a.x_dtype == 1 ? launch_gemv_y<M, true, true>(a) : launch_gemv_y<M, false, true>(a);
+    return a.x_dtype == 1 ? launch_gemv_y<M, true, false>(a) : launch_gemv_y<M, false, false>(a);
 }
 
 }  // namespace

@@ -12,7 +12,9 @@ struct GemmArgs {
     const void *X;       // [M,K] fp16/bf16
     int x_dtype;         // 0 = fp16, 1 = bf16
     const uint8_t *W;    // [N,K/4]
-    const uint16_t *S;   // [N,K/128] fp16 bits
+    const uint16_t *S;   // [N,K/128] fp16 bits (when Q is null)
+    const int8_t *Q;     // int8 scale codes [N,K/128], or null
+    const float *R;      // per-row factor [N] of the int8 codes (scale = Q * R)
     void *Y;             // [M,N]
     int y_dtype;         // 0 = fp16, 1 = bf16, 2 = fp32
     int64_t M, N, K;
@@ -26,9 +28,13 @@ size_t gemv_lds_bytes(int64_t M, int64_t K);
 
 // Batched path: MFMA GEMM, any M >= 1.
 hipError_t launch_gemm(const GemmArgs &a);
-// Batched path for many rows with fp16 X: 256 x 256 tiles, weights decoded
-// once per workgroup into LDS.
+// Batched path for many rows with fp16 X and fp16 scales: 256 x 256 or
+// 128 x 64 tiles, weights decoded once per workgroup into LDS.
 hipError_t launch_gemm_big(const GemmArgs &a);
+
+// Int8 scale codes: Q[n,g] = rint(S[n,g] / R[n]), R[n] = max_g |S[n,g]| / 127.
+hipError_t launch_quantize_scales(const uint16_t *S, int8_t *Q, float *R, int64_t N, int64_t groups,
+                                  hipStream_t stream);
 
 // W[N,K] = t * s in fp16 (w_dtype 0) or bf16 (1).
 hipError_t launch_dequant(const uint8_t *P, const uint16_t *S, void *W, int w_dtype, int64_t N, int64_t K,

@@ -114,6 +114,51 @@ def dequant(packed: torch.Tensor, scales: torch.Tensor, out_dtype: torch.dtype =
     return out
 
 
+# --- int8 block scales -------------------------------------------------------
+
+def quantize_scales(scales: torch.Tensor, group: int = 128):
+    """fp16 scales [N,G] -> (int8 codes [N,G], fp32 row factors [N]); scale = q * r."""
+    _need(scales, "scales", torch.float16)
+    N, G = scales.shape
+    q = torch.empty((N, G), dtype=torch.int8, device=scales.device)
+    r = torch.empty((N,), dtype=torch.float32, device=scales.device)
+    _check(lib.tern_quantize_scales(scales.data_ptr(), q.data_ptr(), r.data_ptr(), N, G * group, group,
+                                    _stream(scales)), "tern_quantize_scales")
+    return q, r
+
+
+def matmul_s8_into(x: torch.Tensor, packed: torch.Tensor, scales_q: torch.Tensor, row_factor: torch.Tensor,
+                   out: torch.Tensor, group: int = 128, path: str = "auto") -> torch.Tensor:
+    """out[M,N] = x . (T * (q * r))^T with int8 block codes q [N,K/group] and row factors r [N]."""
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    _need(x, "x", x.dtype)
+    _need(packed, "packed", torch.uint8)
+    _need(scales_q, "scales_q", torch.int8)
+    _need(row_factor, "row_factor", torch.float32, ndim=1)
+    if out.dtype not in _TORCH_CODE:
+        raise TypeError("out must be float32, bfloat16 or float16")
+    _need(out, "out", out.dtype)
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K or tuple(scales_q.shape) != (N, K // group if group > 0 else 0) \
+            or tuple(row_factor.shape) != (N,) or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, packed {tuple(packed.shape)}, "
+                         f"scales_q {tuple(scales_q.shape)}, row_factor {tuple(row_factor.shape)}, "
+                         f"out {tuple(out.shape)}")
+    st = lib.tern_matmul_s8(x.data_ptr(), _TORCH_CODE[x.dtype], packed.data_ptr(), scales_q.data_ptr(),
+                            row_factor.data_ptr(), out.data_ptr(), _TORCH_CODE[out.dtype], M, N, K, group,
+                            _PATHS[path], _stream(x))
+    _check(st, "tern_matmul_s8")
+    return out
+
+
+def matmul_s8(x: torch.Tensor, packed: torch.Tensor, scales_q: torch.Tensor, row_factor: torch.Tensor,
+              out_dtype: torch.dtype = torch.bfloat16, group: int = 128, path: str = "auto") -> torch.Tensor:
+    out = torch.empty((x.shape[0], packed.shape[0]), dtype=out_dtype, device=x.device)
+    return matmul_s8_into(x, packed, scales_q, row_factor, out, group, path)
+
+
 # --- one GPU's share of a sharded layer (no communication here) -------------
 
 def shard_columns(packed: torch.Tensor, scales: torch.Tensor, rank: int, world: int):

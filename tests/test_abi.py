@@ -102,3 +102,38 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def mm8(X=P, xd=BF16, W=P, Q=P, R=P, Y=P, yd=F32, M=1, N=16, K=128, G=128, path=0):
+    return L.tern_matmul_s8(X, xd, W, Q, R, Y, yd, M, N, K, G, path, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), SHAPE), (dict(K=130), SHAPE), (dict(K=192), GROUP), (dict(K=256, G=64), UNSUP),
+    (dict(xd=F32), DTYPE), (dict(yd=9), DTYPE),
+    (dict(X=0), NULL), (dict(W=0), NULL), (dict(Q=0), NULL), (dict(R=0), NULL), (dict(Y=0), NULL),
+    (dict(X=P + 8), ALIGN), (dict(W=P + 4), ALIGN), (dict(R=P + 2), ALIGN), (dict(Y=P + 2), ALIGN),
+    (dict(M=5, path=1), UNSUP), (dict(path=3), UNSUP),
+])
+def test_matmul_s8_rejects(kw, want):
+    assert mm8(**kw) == want
+
+
+def test_matmul_s8_codes_need_no_alignment_and_empty_is_ok():
+    # int8 codes may start at any byte: an odd code pointer passes the
+    # alignment check, so the NULL row factor checked after it is reported
+    assert mm8(Q=P + 1, R=0) == NULL
+    assert mm8(X=0, W=0, Q=0, R=0, Y=0, M=0) == OK
+
+
+def test_quantize_scales_rejects():
+    f = L.tern_quantize_scales
+    assert f(P, P, P, -1, 128, 128, None) == SHAPE
+    assert f(P, P, P, 4, 192, 128, None) == GROUP
+    assert f(P, P, P, 4, 256, 64, None) == UNSUP
+    assert f(0, P, P, 4, 128, 128, None) == NULL
+    assert f(P, 0, P, 4, 128, 128, None) == NULL
+    assert f(P, P, 0, 4, 128, 128, None) == NULL
+    assert f(P + 1, P, P, 4, 128, 128, None) == ALIGN
+    assert f(P, P, P + 2, 4, 128, 128, None) == ALIGN
+    assert f(0, 0, 0, 0, 128, 128, None) == OK
