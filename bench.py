@@ -286,6 +286,39 @@ def int8_scale_variant():
     return res
 
 
+def zero_block_skip(rate: float = 0.5):
+    """Dense tern_matmul vs tern_matmul_blockmap on decode shapes whose weights have a
+    fraction `rate` of all-zero 128-weight blocks (and on the dense weights, rate 0,
+    for the skipping kernel's overhead); weights rotated over 1 GB."""
+    import numpy as np
+    import torch
+
+    import ternary_weight_matmul_amd as tern
+    import workloads
+
+    res = []
+    for cid, si in ((2, 0), (3, 0), (3, 1), (3, 2)):
+        for r in (0.0, rate):
+            p = workloads.make_problem(cid, si)
+            sh = p.shape
+            if r > 0:
+                p.packed = workloads.draw_block_sparse_packed(workloads.rng_for(cid, 50, si), sh.N, sh.K, r,
+                                                              workloads.CONFIGS[cid].code_probs)
+            x, ws, ss, y, copies, _ = _device_problem(p, 1.0)
+            maps = [tern.block_map(w) for w in ws]
+            marked = float(np.unpackbits(maps[0].cpu().numpy().view(np.uint8)).sum()) / (sh.N * (sh.K // 128))
+            t_dense = _graph_time_ms(lambda i: tern.matmul_into(x, ws[i % copies], ss[i % copies], y), 500, 10)
+            t_skip = _graph_time_ms(lambda i: tern.matmul_blockmap_into(x, ws[i % copies], ss[i % copies],
+                                                                        maps[i % copies], y), 500, 10)
+            res.append({"workload": f"{workloads.CONFIGS[cid].name} M={sh.M} K={sh.K} N={sh.N}",
+                        "zero_block_rate": r, "marked_fraction": round(marked, 4),
+                        "dense_us": round(t_dense * 1e3, 3), "skip_us": round(t_skip * 1e3, 3),
+                        "skip_over_dense": round(t_skip / t_dense, 4)})
+            del x, ws, ss, y, maps
+            torch.cuda.empty_cache()
+    return res
+
+
 def decode_sweep(reps: int = 3):
     """One token through 48 layers x 7 projections at M=1 (q, k, v, o 5120->5120; gate, up
     5120->17408; down 17408->5120): 336 launches over distinct weights captured in one graph."""
@@ -442,6 +475,7 @@ def main():
         out["decode_sweep"] = decode_sweep()
         torch.cuda.empty_cache()
         out["int8_scales"] = int8_scale_variant()
+        out["zero_block_skip"] = zero_block_skip()
         out["other_workloads"] = other_workloads((args.config, args.shape))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)

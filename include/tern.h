@@ -132,6 +132,33 @@ tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W,
                          int64_t N, int64_t K, int32_t group, hipStream_t stream);
 
 /*
+ * tern_block_map -- which 128-weight blocks hold a nonzero weight.
+ * Source: 2kiu.com/news/5082861 §6 (next steps: skip blocks that are
+ * entirely zero).  block_map[n, w] (uint32, row-major [N, ceil(K/4096)]) has
+ * bit b set when block 32w + b of row n contains a code 01 or 10; blocks of
+ * codes 00 and 11 only are clear, and so are the unused high bits of a row's
+ * last word.  packed 16-byte aligned, block_map 4-byte aligned; group must
+ * be 128.  Computed once per weight matrix, not per product.
+ */
+tern_status tern_block_map(const uint8_t *packed, uint32_t *block_map, int64_t N, int64_t K, int32_t group,
+                           hipStream_t stream);
+
+/*
+ * tern_matmul_blockmap -- tern_matmul that skips the unmarked blocks.
+ * Source: 2kiu.com/news/5082861 §6 (zero-block skipping), §4.2 otherwise.
+ * Same arguments, layouts, result contract and errors as tern_matmul, plus
+ * block_map in the layout of tern_block_map (4-byte aligned; NULL only when
+ * M, N or K is 0).  Blocks whose bit is clear are not read (no code bytes,
+ * no scale) and not computed, so the map must mark every block with a
+ * nonzero weight; marking more blocks is harmless.  The skipping kernel is
+ * the decode path (1 <= M <= TERN_GEMV_MAX_M); other calls are tern_matmul
+ * (the map is not read).
+ */
+tern_status tern_matmul_blockmap(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
+                                 const uint16_t *scales, const uint32_t *block_map, void *Y, tern_dtype y_dtype,
+                                 int64_t M, int64_t N, int64_t K, int32_t group, hipStream_t stream);
+
+/*
  * tern_quantize_scales -- int8 scale codes for tern_matmul_s8.
  * Source: 2kiu.com/news/5082861 §6 (next steps: compress the fp16 block
  * scale further to INT8).  The pages do not fix the scheme; this library's

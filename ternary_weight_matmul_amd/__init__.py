@@ -23,8 +23,8 @@ from ._lib import (  # noqa: F401
     lib,
     library_path,
 )
-from .ops import (dequant, matmul, matmul_into, matmul_s8, matmul_s8_into, pack, quantize_scales,  # noqa: F401
-                  shard_columns, shard_k, unpack)
+from .ops import (block_map, dequant, matmul, matmul_blockmap, matmul_blockmap_into, matmul_into,  # noqa: F401
+                  matmul_s8, matmul_s8_into, pack, quantize_scales, shard_columns, shard_k, unpack)
 
 GROUP = 128
 GEMV_MAX_M = 4

@@ -44,7 +44,7 @@ def _load() -> ctypes.CDLL:
     path = library_path()
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is not built; run `python -m ternary_weight_matmul_amd.build` "
+            f"{path} is not built; run `python ternary_weight_matmul_amd/build.py` "
             "(hipcc --offload-arch=gfx950). There is no non-HIP fallback.")
     L = ctypes.CDLL(path)
     i64, vp, i32, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
@@ -62,6 +62,10 @@ def _load() -> ctypes.CDLL:
     L.tern_matmul_path.restype = c_int
     L.tern_dequant.argtypes = [vp, vp, vp, c_int, i64, i64, i32, vp]
     L.tern_dequant.restype = c_int
+    L.tern_block_map.argtypes = [vp, vp, i64, i64, i32, vp]
+    L.tern_block_map.restype = c_int
+    L.tern_matmul_blockmap.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, i64, i64, i64, i32, vp]
+    L.tern_matmul_blockmap.restype = c_int
     L.tern_quantize_scales.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.tern_quantize_scales.restype = c_int
     L.tern_matmul_s8.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, i64, i64, i64, i32, c_int, vp]

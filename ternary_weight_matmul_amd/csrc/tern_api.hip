@@ -164,6 +164,45 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 
+tern_status tern_block_map(const uint8_t *packed, uint32_t *block_map, int64_t N, int64_t K, int32_t group,
+                           hipStream_t stream) {
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxK || !product_ok(N, K) || K % 4 != 0) return TERN_ERR_SHAPE;
+    if (group <= 0 || K % group != 0) return TERN_ERR_GROUP;
+    if (group != TERN_GROUP) return TERN_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return TERN_OK;
+    if (packed == nullptr || block_map == nullptr) return TERN_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(block_map, 4)) return TERN_ERR_ALIGN;
+    return from_hip(tern::launch_block_map(packed, block_map, N, K, stream));
+}
+
+tern_status tern_matmul_blockmap(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
+                                 const uint16_t *scales, const uint32_t *block_map, void *Y, tern_dtype y_dtype,
+                                 int64_t M, int64_t N, int64_t K, int32_t group, hipStream_t stream) {
+    const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales, 2, Y, y_dtype, M, N, K, group);
+    if (st != TERN_OK) return st;
+    if (M > 0 && N > 0 && K > 0 && block_map == nullptr) return TERN_ERR_NULL;
+    if (!aligned(block_map, 4)) return TERN_ERR_ALIGN;
+    const bool skip = M >= 1 && M <= TERN_GEMV_MAX_M && K > 0 && tern::gemv_skip_lds_bytes(M, K) <= kGemvLdsLimit;
+    if (!skip) return tern_matmul_path(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group, TERN_PATH_AUTO,
+                                       stream);
+    if (N == 0) return TERN_OK;
+
+    tern::GemmArgs a;
+    a.X = X;
+    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
+    a.W = packed_W;
+    a.S = scales;
+    a.Q = nullptr;
+    a.R = nullptr;
+    a.Y = Y;
+    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.stream = stream;
+    return from_hip(tern::launch_gemv_skip(a, block_map));
+}
+
 tern_status tern_dequant(const uint8_t *packed, const uint16_t *scales, void *W, tern_dtype w_dtype,
                          int64_t N, int64_t K, int32_t group, hipStream_t stream) {
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxK || !product_ok(N, K) || K % 4 != 0) return TERN_ERR_SHAPE;

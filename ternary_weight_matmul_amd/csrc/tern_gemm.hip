@@ -152,10 +152,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 
     uint2 w0[NB], w1[NB];
     uint32_t s0[NB], s1[NB];    // fp16 scale bits, or the sign-extended int8 code
-    float rowf[NB];             // S8: half the row factor of this lane's column
+    float rowf[NB];             // S8: the row factor of this lane's column, applied in the epilogue
     if constexpr (S8) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) rowf[nb] = R[min(n0 + nb * 16 + li, N - 1)] * 0.5f;
+        for (int nb = 0; nb < NB; ++nb) rowf[nb] = R[min(n0 + nb * 16 + li, N - 1)];
     }
     load_a(0);
     load_w(0, w0, s0);
@@ -215,8 +215,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             // block boundary: scale the block's sums (s/2: the operands were +-2)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float s = S8 ? (float)(int32_t)s0[nb] * rowf[nb]
-                                   : f16_bits_to_float((uint16_t)s0[nb]) * 0.5f;
+                const float s = (S8 ? (float)(int32_t)s0[nb] : f16_bits_to_float((uint16_t)s0[nb])) * 0.5f;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     acc[mb][nb][0] = fmaf(s, part[mb][nb][0], acc[mb][nb][0]);
@@ -276,7 +275,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + mb * 16 + lg * 4 + i;
-                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, acc[mb][nb][i]);
+                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, S8 ? acc[mb][nb][i] * rowf[nb] : acc[mb][nb][i]);
             }
         }
 }

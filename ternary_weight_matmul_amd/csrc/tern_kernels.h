@@ -26,6 +26,13 @@ hipError_t launch_gemv(const GemmArgs &a);
 // LDS bytes the GEMV needs for this M, K (it stages X[M,K] on chip).
 size_t gemv_lds_bytes(int64_t M, int64_t K);
 
+// Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 4).
+hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map);
+size_t gemv_skip_lds_bytes(int64_t M, int64_t K);
+
+// MAP[n, w] bit b = block 32w + b of row n holds a nonzero weight.
+hipError_t launch_block_map(const uint8_t *P, uint32_t *map, int64_t N, int64_t K, hipStream_t stream);
+
 // Batched path: MFMA GEMM, any M >= 1.
 hipError_t launch_gemm(const GemmArgs &a);
 // Batched path for many rows with fp16 X and fp16 scales: 256 x 256 or

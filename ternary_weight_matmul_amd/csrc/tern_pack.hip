@@ -1,4 +1,4 @@
-// tern_pack.hip -- packed-layout utilities: pack, unpack, zero fill.
+// tern_pack.hip -- packed-layout utilities: pack, unpack, block map, zero fill.
 //
 // Layout (2kiu.com/news/5082861 §3.1): weight 4j+i of a row lives in bits
 // 2i..2i+1 of byte j of that row, codes 00 -> 0, 01 -> +1, 10 -> -1,
@@ -78,6 +78,32 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ P, int8_t *__restrict_
     }
 }
 
+// Block map: one thread per map word (32 blocks of 128 weights = 32 x 32
+// bytes of one row).  A code is a nonzero weight exactly when its two bits
+// differ (01 or 10), so a block is marked when (w ^ (w >> 1)) & 0x5555...
+// is nonzero for any of its eight 32-bit words.
+__global__ void block_map_kernel(const uint8_t *__restrict__ P, uint32_t *__restrict__ map, int64_t N,
+                                 int64_t groups, int64_t words) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t row_bytes = groups * 32;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N * words; i += stride) {
+        const int64_t n = i / words;
+        const int64_t g0 = (i - n * words) * 32;
+        const int64_t g1 = min(g0 + 32, groups);
+        uint32_t bits = 0;
+        for (int64_t g = g0; g < g1; ++g) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(P + n * row_bytes + g * 32);
+            const uint4 a = src[0];
+            const uint4 b = src[1];
+            const uint32_t any = ((a.x ^ (a.x >> 1)) | (a.y ^ (a.y >> 1)) | (a.z ^ (a.z >> 1)) |
+                                  (a.w ^ (a.w >> 1)) | (b.x ^ (b.x >> 1)) | (b.y ^ (b.y >> 1)) |
+                                  (b.z ^ (b.z >> 1)) | (b.w ^ (b.w >> 1))) & 0x55555555u;
+            if (any) bits |= 1u << (g - g0);
+        }
+        map[i] = bits;
+    }
+}
+
 __global__ void fill_zero_kernel(uint8_t *__restrict__ Y, int64_t bytes) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes; i += stride) Y[i] = 0;
@@ -103,6 +129,15 @@ hipError_t launch_unpack(const uint8_t *P, int8_t *T, int64_t n_bytes, hipStream
     const int block = 256;
     hipLaunchKernelGGL(unpack_kernel, dim3(grid_for((n_bytes >> 2) + 1, block)), dim3(block), 0, stream, P, T,
                        n_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_map(const uint8_t *P, uint32_t *map, int64_t N, int64_t K, hipStream_t stream) {
+    const int block = 256;
+    const int64_t groups = K / 128;
+    const int64_t words = (groups + 31) / 32;
+    hipLaunchKernelGGL(block_map_kernel, dim3(grid_for(N * words, block)), dim3(block), 0, stream, P, map, N,
+                       groups, words);
     return hipGetLastError();
 }
 

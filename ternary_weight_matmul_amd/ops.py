@@ -114,6 +114,52 @@ def dequant(packed: torch.Tensor, scales: torch.Tensor, out_dtype: torch.dtype =
     return out
 
 
+# --- zero-block skipping -----------------------------------------------------
+
+def block_map(packed: torch.Tensor, group: int = 128) -> torch.Tensor:
+    """packed [N,K/4] -> int32 [N, ceil(K/group/32)], the bits of tern_block_map (stored as int32)."""
+    _need(packed, "packed", torch.uint8)
+    N = packed.shape[0]
+    K = packed.shape[1] * 4
+    words = (K // group + 31) // 32
+    out = torch.empty((N, words), dtype=torch.int32, device=packed.device)
+    _check(lib.tern_block_map(packed.data_ptr(), out.data_ptr(), N, K, group, _stream(packed)),
+           "tern_block_map")
+    return out
+
+
+def matmul_blockmap_into(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, bmap: torch.Tensor,
+                         out: torch.Tensor, group: int = 128) -> torch.Tensor:
+    """matmul_into that skips the blocks `bmap` (from block_map) leaves unmarked."""
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    _need(x, "x", x.dtype)
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.float16)
+    _need(bmap, "bmap", torch.int32)
+    if out.dtype not in _TORCH_CODE:
+        raise TypeError("out must be float32, bfloat16 or float16")
+    _need(out, "out", out.dtype)
+    M, K = x.shape
+    N = packed.shape[0]
+    words = (K // group + 31) // 32 if group > 0 else 0
+    if packed.shape[1] * 4 != K or tuple(scales.shape) != (N, K // group if group > 0 else 0) \
+            or tuple(bmap.shape) != (N, words) or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, packed {tuple(packed.shape)}, "
+                         f"scales {tuple(scales.shape)}, bmap {tuple(bmap.shape)}, out {tuple(out.shape)}")
+    st = lib.tern_matmul_blockmap(x.data_ptr(), _TORCH_CODE[x.dtype], packed.data_ptr(), scales.data_ptr(),
+                                  bmap.data_ptr(), out.data_ptr(), _TORCH_CODE[out.dtype], M, N, K, group,
+                                  _stream(x))
+    _check(st, "tern_matmul_blockmap")
+    return out
+
+
+def matmul_blockmap(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, bmap: torch.Tensor,
+                    out_dtype: torch.dtype = torch.bfloat16, group: int = 128) -> torch.Tensor:
+    out = torch.empty((x.shape[0], packed.shape[0]), dtype=out_dtype, device=x.device)
+    return matmul_blockmap_into(x, packed, scales, bmap, out, group)
+
+
 # --- int8 block scales -------------------------------------------------------
 
 def quantize_scales(scales: torch.Tensor, group: int = 128):

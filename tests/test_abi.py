@@ -137,3 +137,31 @@ def test_quantize_scales_rejects():
     assert f(P + 1, P, P, 4, 128, 128, None) == ALIGN
     assert f(P, P, P + 2, 4, 128, 128, None) == ALIGN
     assert f(0, 0, 0, 0, 128, 128, None) == OK
+
+
+def test_block_map_rejects():
+    f = L.tern_block_map
+    assert f(P, P, -1, 128, 128, None) == SHAPE
+    assert f(P, P, 4, 130, 128, None) == SHAPE
+    assert f(P, P, 4, 192, 128, None) == GROUP
+    assert f(P, P, 4, 256, 64, None) == UNSUP
+    assert f(0, P, 4, 128, 128, None) == NULL
+    assert f(P, 0, 4, 128, 128, None) == NULL
+    assert f(P + 8, P, 4, 128, 128, None) == ALIGN
+    assert f(P, P + 2, 4, 128, 128, None) == ALIGN
+    assert f(0, 0, 0, 128, 128, None) == OK
+    assert f(0, 0, 4, 0, 128, None) == OK
+
+
+def mmb(X=P, xd=BF16, W=P, S=P, MAP=P, Y=P, yd=F32, M=1, N=16, K=128, G=128):
+    return L.tern_matmul_blockmap(X, xd, W, S, MAP, Y, yd, M, N, K, G, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), SHAPE), (dict(K=130), SHAPE), (dict(K=192), GROUP), (dict(K=256, G=64), UNSUP),
+    (dict(xd=F32), DTYPE), (dict(X=0), NULL), (dict(S=0), NULL), (dict(MAP=0), NULL), (dict(Y=0), NULL),
+    (dict(S=P + 1), ALIGN), (dict(MAP=P + 2), ALIGN), (dict(X=P + 8), ALIGN),
+])
+def test_matmul_blockmap_rejects(kw, want):
+    assert mmb(**kw) == want
+    assert mmb(X=0, W=0, S=0, MAP=0, Y=0, M=0) == OK
