@@ -7,19 +7,22 @@
 // on chip, never re-read from memory in the inner loop (§4.2, §4.3); wide
 // vector loads of the packed bytes (§4.3, third version).
 //
-// Work layout (one workgroup = 16 output rows x all of K):
-//   * a wave "step" covers 16 rows x 1024 weights: lane = 16*r + kk; for
-//     j = 0..3 the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
+// Work layout (one workgroup = 4 JR output rows x all of K; JR = 1 or 2):
+//   * a wave "step" covers 4 JR rows x 1024 weights: lane = 16*r + kk; for
+//     j < JR the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
 //     offset step*1024 + 64*kk, so every load instruction reads four
 //     256-byte contiguous row segments;
-//   * the waves of a workgroup (up to 16 for M = 1, 8 otherwise) split the K steps.  Each wave first issues all
-//     of its weight and scale loads, then stages the activations of its own
-//     steps into a wave-private LDS slice (pair-interleaved, see
-//     tern_device.h; the four lanes that share a 64-weight chunk stage a
-//     quarter each), then decodes and accumulates as the loads land;
+//   * the waves of a workgroup (up to 16 for M = 1, 8 otherwise) split the K
+//     steps.  Each wave first issues all of its weight and scale loads, then
+//     stages the activations of its own steps into a wave-private LDS slice
+//     (pair-interleaved, see tern_device.h; the four lanes that share a
+//     64-weight chunk stage a quarter each), then decodes and accumulates as
+//     the loads land;
 //   * each lane keeps one fp32 partial per (row, m); it is summed over the
 //     16 lanes of its DPP row, then across the waves through LDS in a fixed
 //     order (deterministic; no atomics, no workspace).
+//   * small workgroups (8 rows, or 4 when K > 16384 at M = 1) spread a
+//     layer's rows over many CUs, so no CU runs much more than its share.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -32,7 +35,7 @@ namespace tern {
 
 namespace {
 
-constexpr int ROWS = 16;          // output rows per workgroup
+constexpr int SKIP_ROWS = 16;     // rows per workgroup of the zero-block skipping kernel
 constexpr int STEP = 1024;        // weights of one row per wave step
 constexpr int CHUNK = 64;         // weights per lane per row per step (16 bytes)
 constexpr int PIECES = 128;       // 16-byte activation pieces per (step, m): 16 chunks x 8
@@ -71,13 +74,15 @@ __device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M
 
 // S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N]
 // (the int8-scale variant) instead of fp16 values S[N,K/128].
-template <int M, bool XBF16, int YT, int SPW, bool S8>
+// JR: rows per 16-lane team; a workgroup covers ROWS = 4 JR rows.
+template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
                                                      const int8_t *__restrict__ Q,
                                                      const float *__restrict__ R,
                                                      void *__restrict__ Y, int N, int K) {
+    constexpr int ROWS = 4 * JR;
     extern __shared__ uint4 lds[];
     const int nsteps = (K + STEP - 1) / STEP;
     const int tid = threadIdx.x;
@@ -113,13 +118,13 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
             xraw[si][m][1] = src[1];
         }
     }
-    uint4 code[SPW][4];
-    uint32_t sbits[SPW][4];     // fp16 scale bits, or the sign-extended int8 code
+    uint4 code[SPW][JR];
+    uint32_t sbits[SPW][JR];     // fp16 scale bits, or the sign-extended int8 code
 #pragma unroll
     for (int si = 0; si < SPW; ++si) {
         const int c = min((s_begin + si) * 16 + kk, nchunks - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < JR; ++j) {
             const int64_t n = min(n0 + 4 * j + r, N - 1);
             code[si][j] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
             if constexpr (S8) sbits[si][j] = (uint32_t)(int32_t)Q[n * groups + (c >> 1)];
@@ -151,9 +156,9 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- 3. decode + sign-select accumulate, scale at the block boundary ----
-    float acc[4][M];
+    float acc[JR][M];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JR; ++j)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
 
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
                 for (int q = 0; q < 8; ++q) xq[m][q] = src[q * 16 + kk];
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JR; ++j) {
                 // this lane's 64 weights lie inside one 128-weight block; the +-2
                 // operands double the sum and the 0.5 undoes it exactly
                 float part[MC];
@@ -196,12 +201,12 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
 
     // ---- 4. reduce over the 16 lanes of each DPP row, then across waves ----
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JR; ++j)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[j][m] = row16_sum(acc[j][m]);
     if (kk == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JR; ++j)
 #pragma unroll
             for (int m = 0; m < M; ++m) red[(wave * ROWS + 4 * j + r) * M + m] = acc[j][m];
     }
@@ -242,13 +247,13 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const ui
     const int nwaves = blockDim.x >> 6;
     const int r = lane >> 4;
     const int kk = lane & 15;
-    const int n0 = blockIdx.x * ROWS;
+    const int n0 = blockIdx.x * SKIP_ROWS;
     const int64_t row_bytes = K >> 2;
     const int groups = K >> 7;
     const int mapw = (groups + 31) >> 5;
     uint4 *xw = lds + wave * (SPW * M * PIECES);
     float *red = reinterpret_cast<float *>(lds + nwaves * (SPW * M * PIECES));
-    uint8_t *slots = reinterpret_cast<uint8_t *>(red + nwaves * ROWS * M) + wave * (SPW * 4 * 64);
+    uint8_t *slots = reinterpret_cast<uint8_t *>(red + nwaves * SKIP_ROWS * M) + wave * (SPW * 4 * 64);
     const int s_begin = wave * SPW;
     const int nchunks = K / CHUNK;
 
@@ -367,21 +372,21 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const ui
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int m = 0; m < M; ++m) red[(wave * ROWS + 4 * j + r) * M + m] = acc[j][m];
+            for (int m = 0; m < M; ++m) red[(wave * SKIP_ROWS + 4 * j + r) * M + m] = acc[j][m];
     }
     __syncthreads();
-    if (tid < ROWS * M) {
-        const int row = tid % ROWS;
-        const int m = tid / ROWS;
+    if (tid < SKIP_ROWS * M) {
+        const int row = tid % SKIP_ROWS;
+        const int m = tid / SKIP_ROWS;
         float y = 0.f;
-        for (int w = 0; w < nwaves; ++w) y += red[(w * ROWS + row) * M + m];
+        for (int w = 0; w < nwaves; ++w) y += red[(w * SKIP_ROWS + row) * M + m];
         const int n = n0 + row;
         if (n < N) store_out<YT>(Y, (int64_t)m * N + n, y);
     }
 }
 
 struct GemvShape {
-    int nsteps, spw, nwaves;
+    int nsteps, spw, nwaves, jr;
     size_t lds;
 };
 
@@ -392,13 +397,19 @@ GemvShape gemv_shape(int64_t M, int64_t K) {
     g.spw = (g.nsteps + max_waves - 1) / max_waves;
     if (g.spw < 1) g.spw = 1;
     g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
-    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * ROWS * M * sizeof(float);
+    // rows per team: 2 (8-row workgroups); 1 when one row's K already gives
+    // every wave two steps (M = 1, K > 16384).  Measured on the decode shapes:
+    // fewer rows per workgroup spread the rows of a layer over more CUs.
+    g.jr = (M == 1 && g.spw >= 2) ? 1 : 2;
+    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * g.jr * M * sizeof(float);
     return g;
 }
 
-template <int M, bool XBF16, int YT, int SPW, bool S8>
+template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
-    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8>;
+    constexpr int ROWS = 4 * JR;
+    if (g.jr != JR) return hipErrorInvalidValue;   // the LDS size was computed for g.jr
+    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8, JR>;
     if (g.lds > 64 * 1024) {
         // raise the dynamic-LDS limit once per device (not a stream operation,
         // so it is kept out of any graph capture after the first call)
@@ -425,14 +436,14 @@ template <int M, bool XBF16, int YT, bool S8>
 hipError_t launch_gemv_s(const GemmArgs &a) {
     const GemvShape g = gemv_shape(M, a.K);
     if constexpr (M == 1) {   // gemv_lds_bytes admits at most two steps per wave for M = 1
-        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
-        return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
+        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
+        return launch_gemv_t<M, XBF16, YT, 2, S8, 1>(a, g);
     } else {
         switch (g.spw) {
-        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
-        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
-        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8>(a, g);
-        default: return launch_gemv_t<M, XBF16, YT, 4, S8>(a, g);
+        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
+        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8, 2>(a, g);
+        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8, 2>(a, g);
+        default: return launch_gemv_t<M, XBF16, YT, 4, S8, 2>(a, g);
         }
     }
 }
@@ -452,13 +463,17 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
     return a.x_dtype == 1 ? launch_gemv_y<M, true, false>(a) : launch_gemv_y<M, false, false>(a);
 }
 
-// bytes of the per-wave item lists of the skipping kernel
-size_t skip_list_bytes(const GemvShape &g) { return (size_t)g.nwaves * g.spw * 4 * 64; }
+// LDS of the skipping kernel: staged activations, its 16-row reduction
+// buffer and the per-wave item lists
+size_t skip_lds(const GemvShape &g, int64_t M) {
+    return (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * SKIP_ROWS * M * sizeof(float) +
+           (size_t)g.nwaves * g.spw * 4 * 64;
+}
 
 template <int M, bool XBF16, int YT, int SPW>
 hipError_t launch_skip_t(const GemmArgs &a, const uint32_t *map, const GemvShape &g) {
     auto kern = gemv_skip_kernel<M, XBF16, YT, SPW>;
-    const size_t lds = g.lds + skip_list_bytes(g);
+    const size_t lds = skip_lds(g, M);
     if (lds > 64 * 1024) {
         static std::atomic<uint64_t> done_mask{0};
         int dev = 0;
@@ -472,7 +487,7 @@ hipError_t launch_skip_t(const GemmArgs &a, const uint32_t *map, const GemvShape
             done_mask.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
-    const dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
+    const dim3 grid((unsigned)((a.N + SKIP_ROWS - 1) / SKIP_ROWS));
     const dim3 block((unsigned)(64 * g.nwaves));
     hipLaunchKernelGGL(kern, grid, block, lds, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, map, a.Y,
                        (int)a.N, (int)a.K);
@@ -512,9 +527,8 @@ hipError_t launch_skip_m(const GemmArgs &a, const uint32_t *map) {
 }  // namespace
 
 size_t gemv_skip_lds_bytes(int64_t M, int64_t K) {
-    const size_t dense = gemv_lds_bytes(M, K);
-    if (dense == (size_t)-1) return dense;
-    return dense + skip_list_bytes(gemv_shape(M, K));
+    if (gemv_lds_bytes(M, K) == (size_t)-1) return (size_t)-1;
+    return skip_lds(gemv_shape(M, K), M);
 }
 
 hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map) {
