@@ -202,6 +202,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         __builtin_amdgcn_sched_barrier(0);
         store_w(buf ^ 1, wc, sb);
         mfmas();
+        // spread the decode between the first half's MFMAs (they read only
+        // fragments loaded above), so the SIMD's other wave can issue its
+        // MFMAs while this one decodes, and vice versa
+#pragma unroll
+        for (int i = 0; i < MB * NB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
         read_frags(buf, f1);
         mfmas();
         __syncthreads();
