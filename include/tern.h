@@ -56,7 +56,7 @@ typedef enum { TERN_F16 = 0, TERN_BF16 = 1, TERN_F32 = 2 } tern_dtype;
 
 /* Which kernel family computes tern_matmul_path's result. */
 typedef enum {
-    TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does) */
+    TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): GEMV for M <= 2, else MFMA */
     TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
     TERN_PATH_MFMA = 2  /* LDS-staged activations + in-register weight decode + MFMA; any M */
 } tern_path;
@@ -151,8 +151,8 @@ tern_status tern_block_map(const uint8_t *packed, uint32_t *block_map, int64_t N
  * M, N or K is 0).  Blocks whose bit is clear are not read (no code bytes,
  * no scale) and not computed, so the map must mark every block with a
  * nonzero weight; marking more blocks is harmless.  The skipping kernel is
- * the decode path (1 <= M <= TERN_GEMV_MAX_M); other calls are tern_matmul
- * (the map is not read).
+ * the decode path for M <= 2 (where the GEMV is the faster kernel); other
+ * calls are tern_matmul (the map is not read).
  */
 tern_status tern_matmul_blockmap(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
                                  const uint16_t *scales, const uint32_t *block_map, void *Y, tern_dtype y_dtype,

@@ -54,6 +54,15 @@ bool gemv_fits(int64_t M, int64_t K) {
     return M >= 1 && M <= TERN_GEMV_MAX_M && tern::gemv_lds_bytes(M, K) <= kGemvLdsLimit;
 }
 
+// The automatic choice: the VALU decode kernel for one or two activation
+// rows; from three rows on, the MFMA kernel (16-row tiles: its time hardly
+// changes up to M = 16) is faster (measured on the 5120 / 17408 shapes:
+// M = 2 GEMV 7.5-18 us vs MFMA 8.8-22 us; M = 3 about even; M = 4 MFMA
+// 9.0-22.4 us vs GEMV 9.5-27.8 us).
+constexpr int64_t kAutoGemvMaxM = 2;
+
+bool auto_gemv(int64_t M, int64_t K) { return M <= kAutoGemvMaxM && gemv_fits(M, K); }
+
 }  // namespace
 
 extern "C" {
@@ -111,7 +120,7 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
     a.N = N;
     a.K = K;
     a.stream = stream;
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && gemv_fits(M, K));
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 
@@ -160,7 +169,7 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
     a.N = N;
     a.K = K;
     a.stream = stream;
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && gemv_fits(M, K));
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 
@@ -182,7 +191,7 @@ tern_status tern_matmul_blockmap(const void *X, tern_dtype x_dtype, const uint8_
     if (st != TERN_OK) return st;
     if (M > 0 && N > 0 && K > 0 && block_map == nullptr) return TERN_ERR_NULL;
     if (!aligned(block_map, 4)) return TERN_ERR_ALIGN;
-    const bool skip = M >= 1 && M <= TERN_GEMV_MAX_M && K > 0 && tern::gemv_skip_lds_bytes(M, K) <= kGemvLdsLimit;
+    const bool skip = M >= 1 && M <= kAutoGemvMaxM && K > 0 && tern::gemv_skip_lds_bytes(M, K) <= kGemvLdsLimit;
     if (!skip) return tern_matmul_path(X, x_dtype, packed_W, scales, Y, y_dtype, M, N, K, group, TERN_PATH_AUTO,
                                        stream);
     if (N == 0) return TERN_OK;

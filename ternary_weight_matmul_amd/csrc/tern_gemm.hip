@@ -294,7 +294,7 @@ hipError_t launch_t(const GemmArgs &a) {
 
 template <bool XBF16, int YT, bool S8>
 hipError_t launch_shape(const GemmArgs &a) {
-    if (a.M <= 16) return launch_t<1, 2, 2, 4, XBF16, YT, S8>(a);        // 16 x 64 tiles, K split over 4 waves
+    if (a.M <= 16) return launch_t<1, 2, 1, 8, XBF16, YT, S8>(a);        // 16 x 32 tiles, K split over 8 waves
     else return launch_t<4, 4, 4, 1, XBF16, YT, S8>(a);                  // 64 x 256
 }
 

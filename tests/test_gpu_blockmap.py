@@ -72,9 +72,10 @@ def test_skip_matches_oracle(M, K, N, rate):
 
 
 # K a multiple of 1024 (whole wave steps): with a partial last step the list
-# hands its chunks to other lanes, and the 16-lane sum associates differently
-@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 5120, 512, "bf16", "bf16"), (3, 2048, 77, "f16", "f16"),
-                                         (4, 17408, 40, "bf16", "f32"), (2, 3072, 50, "f16", "f32")])
+# hands its chunks to other lanes, and the 16-lane sum associates differently.
+# The skipping kernel serves M <= 2; from M = 3 on the call is tern_matmul.
+@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 5120, 512, "bf16", "bf16"), (2, 2048, 77, "f16", "f16"),
+                                         (1, 17408, 40, "bf16", "f32"), (2, 3072, 50, "f16", "f32")])
 def test_all_marked_equals_dense_kernel_bit_for_bit(M, K, N, xd, yd):
     p = _sparse_problem(M + K + N, M, K, N, 0.5, xd=xd, yd=yd)
     x, w, s = _dev(p)
@@ -84,6 +85,16 @@ def test_all_marked_equals_dense_kernel_bit_for_bit(M, K, N, xd, yd):
     y_dense = tern.matmul(x, w, s, out_dtype=TORCH_DT[yd], path="gemv")
     torch.cuda.synchronize()
     assert np.array_equal(out_bits(y_skip, yd), out_bits(y_dense, yd))
+
+
+@pytest.mark.parametrize("M", [3, 4])
+def test_three_or_more_rows_take_the_dense_product(M):
+    p = _sparse_problem(80 + M, M, 5120, 300, 0.5)
+    x, w, s = _dev(p)
+    y_map = tern.matmul_blockmap(x, w, s, tern.block_map(w), out_dtype=torch.float32)
+    y = tern.matmul(x, w, s, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_map, y)
 
 
 def test_superset_map_is_harmless():
