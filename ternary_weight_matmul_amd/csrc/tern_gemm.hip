@@ -97,7 +97,11 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     const int nkb = K / BK;
     const int niter = (nkb + WK - 1) / WK;
 
-    // ---- activation tile: global -> registers (clamped, unconditional) ----
+    // ---- activation tile: global -> registers (clamped addresses) ----
+    // Rows at or past M are neither loaded nor staged: their LDS rows hold
+    // stale values, which reach only output rows that are never stored (row
+    // i of an MFMA result depends on row i of A alone).  With few activation
+    // rows this cuts the staging work in proportion.
     uint4 a_reg[A_UNITS][2];
     auto load_a = [&](int it) {
 #pragma unroll
@@ -110,15 +114,18 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             const int kb = min(it * WK + w, nkb - 1);
             const int64_t m = min(m0 + row, M - 1);
             const uint4 *src = reinterpret_cast<const uint4 *>(X + m * K + (int64_t)kb * BK + blk * 16);
-            a_reg[u][0] = src[0];
-            a_reg[u][1] = src[1];
+            if (m0 + row < M) {
+                a_reg[u][0] = src[0];
+                a_reg[u][1] = src[1];
+            }
         }
     };
     auto store_a = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
             const int b = tid + NT * u;
-            if (A_UNITS * NT == A_UNITS_TOTAL || b < A_UNITS_TOTAL) {
+            const int rowb = (b - (b / (BM * 8)) * (BM * 8)) >> 3;
+            if ((A_UNITS * NT == A_UNITS_TOTAL || b < A_UNITS_TOTAL) && m0 + rowb < M) {
                 const int w = b / (BM * 8);
                 const int rem = b - w * (BM * 8);
                 const int row = rem >> 3;
