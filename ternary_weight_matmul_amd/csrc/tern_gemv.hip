@@ -40,6 +40,14 @@ constexpr int STEP = 1024;        // weights of one row per wave step
 constexpr int CHUNK = 64;         // weights per lane per row per step (16 bytes)
 constexpr int PIECES = 128;       // 16-byte activation pieces per (step, m): 16 chunks x 8
 
+// 16 code bytes that are read exactly once per product: a non-temporal load
+// (the weights stream through; nothing else reuses their cache lines).
+__device__ __forceinline__ uint4 load_codes(const uint8_t *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Sums of 2t*x over one lane's 64 weights (one 16-byte code vector) against
 // the pair-interleaved activation pieces xq[m][0..7] of the same chunk, for
 // every activation row m: each decoded pair feeds M packed dots.
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
 #pragma unroll
         for (int j = 0; j < JR; ++j) {
             const int64_t n = min(n0 + 4 * j + r, N - 1);
-            code[si][j] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
+            code[si][j] = load_codes(P + n * row_bytes + (int64_t)c * 16);
             if constexpr (S8) sbits[si][j] = (uint32_t)(int32_t)Q[n * groups + (c >> 1)];
             else sbits[si][j] = S[n * groups + (c >> 1)];
         }

@@ -134,6 +134,16 @@ def test_ragged_shapes(M, K, N, xd, yd):
         _full(p, path)
 
 
+@pytest.mark.parametrize("K,N,xd,yd", [(5120, 9001, "bf16", "bf16"), (17408, 5121, "f16", "f32"),
+                                       (5120, 17408, "bf16", "f32"), (1024, 60003, "f16", "f16")])
+def test_decode_rows_beyond_one_round(K, N, xd, yd):
+    """M = 1 with more 8-row workgroups than are resident at once (several
+    rounds), ragged last workgroup included."""
+    p = workloads.make_custom(K + N, 1, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.01)
+    for path in ("auto", "gemv"):
+        _full(p, path)
+
+
 def test_outliers_and_wide_scales():
     # activations with x20 outliers, scales spread over two decades
     p = workloads.make_custom(77, 8, 1024, 96, x_dtype="f16", y_dtype="f32", scale_lo=1e-3, scale_hi=4.0)
@@ -310,7 +320,7 @@ def test_multiple_calls_on_a_side_stream():
 
 
 @pytest.mark.parametrize("M,K,N,xd,yd", [(1, 5120, 640, "bf16", "bf16"), (2, 17408, 96, "bf16", "f32"),
-                                         (300, 1024, 512, "f16", "f16")])
+                                         (300, 1024, 512, "f16", "f16"), (1, 5120, 17408, "bf16", "bf16")])
 def test_hip_graph_replays_match_eager(M, K, N, xd, yd):
     """Captured launches replay to the eager result, every time."""
     p = workloads.make_custom(700 + M, M, K, N, x_dtype=xd, y_dtype=yd)
