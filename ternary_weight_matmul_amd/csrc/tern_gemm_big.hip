@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     constexpr int W_TILE = BN * ROWB;
     constexpr int AP = BM * 8 / NT;          // 16-byte X chunks per thread per step
     constexpr int RSTEP = NT / 8;            // rows between a thread's chunks
-    static_assert(AP * NT == BM * 8 && AP == 4, "four X chunks per thread (kept in scalars)");
+    static_assert(AP * NT == BM * 8 && (AP == 3 || AP == 4), "three or four X chunks per thread (kept in scalars)");
     static_assert(RSTEP % 16 == 0, "swizzle must not depend on the chunk index");
     static_assert(2 * BN <= NT, "one thread per 32 decoded weights");
     // [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     const uint16_t *x_src0 = X + (int64_t)min(m0 + xr, M - 1) * K + xc * 8;
     const uint16_t *x_src1 = X + (int64_t)min(m0 + RSTEP + xr, M - 1) * K + xc * 8;
     const uint16_t *x_src2 = X + (int64_t)min(m0 + 2 * RSTEP + xr, M - 1) * K + xc * 8;
-    const uint16_t *x_src3 = X + (int64_t)min(m0 + 3 * RSTEP + xr, M - 1) * K + xc * 8;
+    const uint16_t *x_src3 = X + (int64_t)min(m0 + (AP > 3 ? 3 : 2) * RSTEP + xr, M - 1) * K + xc * 8;
     const int x_dst = swz(xr, xc);    // + RSTEP*ROWB j (same swizzle)
 
     // W loader: thread t < 2 BN decodes column t/2, weights 32 h .. 32 h + 31 of the step
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         xa0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
         xa1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
         xa2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
-        xa3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
+        if constexpr (AP > 3) xa3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
         wcode = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
         sbits = s_src[s >> 1];
     };
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         *reinterpret_cast<uint4 *>(a_t) = xa0;
         *reinterpret_cast<uint4 *>(a_t + RSTEP * ROWB) = xa1;
         *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = xa2;
-        *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = xa3;
+        if constexpr (AP > 3) *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = xa3;
     };
     auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
         if (w_role) {
@@ -251,15 +251,28 @@ struct Tile {
     }
 };
 
-using Tile256 = Tile<2, 4, 8, 4>;   // 256 x 256, 8 waves of 128 x 64
-using Tile64 = Tile<2, 2, 4, 2>;    // 128 x 64, 4 waves of 64 x 32 (several workgroups per CU)
+using Tile256 = Tile<2, 4, 8, 4>;   // 256 x 256, 8 waves of 128 x 64, one workgroup per CU
+using Tile192 = Tile<2, 4, 6, 4>;   // 192 x 256, 8 waves of 96 x 64, one workgroup per CU
+using Tile64 = Tile<2, 2, 4, 2>;    // 128 x 64, 4 waves of 64 x 32, three workgroups per CU
 
+// Pick the tile with the least estimated time: rounds of resident workgroups
+// times the output area a CU covers per round, divided by the CU throughput
+// measured for that tile (1.0, 0.95, 0.55 relative; 256 CUs).  Quantisation
+// decides most shapes: e.g. 2048 x 17408 is 544 tiles of 256 x 256 (three
+// rounds, the last 71% idle) but 748 of 192 x 256 (three rounds, 97% full).
 template <int YT>
 hipError_t launch_big_y(const GemmArgs &a) {
-    // 256 x 256 tiles run one workgroup per CU: take them while they still
-    // cover three quarters of the 256 CUs, otherwise the small tiles
-    if (Tile256::count(a) >= 192) return Tile256::launch<YT>(a);
-    return Tile64::launch<YT>(a);
+    constexpr int64_t kCUs = 256;
+    auto cost = [&](int64_t tiles, int64_t area, int64_t per_cu, double thr) {
+        const int64_t rounds = (tiles + kCUs * per_cu - 1) / (kCUs * per_cu);
+        return (double)rounds * (double)(area * per_cu) / thr;
+    };
+    const double c256 = cost(Tile256::count(a), 256 * 256, 1, 1.0);
+    const double c192 = cost(Tile192::count(a), 192 * 256, 1, 0.95);
+    const double c64 = cost(Tile64::count(a), 128 * 64, 3, 0.55);
+    if (c64 <= c256 && c64 <= c192) return Tile64::launch<YT>(a);
+    if (c192 < c256) return Tile192::launch<YT>(a);
+    return Tile256::launch<YT>(a);
 }
 
 }  // namespace

@@ -198,10 +198,11 @@ def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
         assert np.array_equal(got, want), (path, np.argwhere(got != want)[:5])
 
 
-@pytest.mark.parametrize("M,K,N,yd", [(2000, 256, 6000, "f16"), (1999, 384, 6001, "f32")])
+@pytest.mark.parametrize("M,K,N,yd", [(2000, 256, 6000, "f16"), (1999, 384, 6001, "f32"), (1000, 128, 17000, "f32")])
 def test_large_tiles_ragged(M, K, N, yd):
-    """Shapes that take the 256 x 256 tiles (at least 192 of them) with
-    ragged row and column tails, compared element by element."""
+    """Shapes that take the 256 x 256 tiles (the first two) and the 192 x 256
+    tiles (the last) with ragged row and column tails, compared element by
+    element."""
     p = workloads.make_custom(M + N, M, K, N, x_dtype="f16", y_dtype=yd, reserved_rate=0.02)
     _full(p, "auto")
 
