@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     constexpr int W_TILE = BN * ROWB;
     constexpr int AP = BM * 8 / NT;          // 16-byte X chunks per thread per step
     constexpr int RSTEP = NT / 8;            // rows between a thread's chunks
-    static_assert(AP * NT == BM * 8 && (AP == 3 || AP == 4), "three or four X chunks per thread (kept in scalars)");
+    static_assert(AP * NT == BM * 8 && AP >= 2 && AP <= 4, "two to four X chunks per thread (kept in scalars)");
     static_assert(RSTEP % 16 == 0, "swizzle must not depend on the chunk index");
     static_assert(2 * BN <= NT, "one thread per 32 decoded weights");
     // [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     const int xc = tid & 7;
     const uint16_t *x_src0 = X + (int64_t)min(m0 + xr, M - 1) * K + xc * 8;
     const uint16_t *x_src1 = X + (int64_t)min(m0 + RSTEP + xr, M - 1) * K + xc * 8;
-    const uint16_t *x_src2 = X + (int64_t)min(m0 + 2 * RSTEP + xr, M - 1) * K + xc * 8;
+    const uint16_t *x_src2 = X + (int64_t)min(m0 + (AP > 2 ? 2 : 1) * RSTEP + xr, M - 1) * K + xc * 8;
     const uint16_t *x_src3 = X + (int64_t)min(m0 + (AP > 3 ? 3 : 2) * RSTEP + xr, M - 1) * K + xc * 8;
     const int x_dst = swz(xr, xc);    // + RSTEP*ROWB j (same swizzle)
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         const int64_t o = (int64_t)s * KS;
         xa0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
         xa1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
-        xa2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
+        if constexpr (AP > 2) xa2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
         if constexpr (AP > 3) xa3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
         wcode = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
         sbits = s_src[s >> 1];
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         uint8_t *a_t = lds + buf * A_TILE + x_dst;
         *reinterpret_cast<uint4 *>(a_t) = xa0;
         *reinterpret_cast<uint4 *>(a_t + RSTEP * ROWB) = xa1;
-        *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = xa2;
+        if constexpr (AP > 2) *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = xa2;
         if constexpr (AP > 3) *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = xa3;
     };
     auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
