@@ -26,63 +26,17 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <type_traits>
 
 #include "tern_device.h"
+#include "tern_gemv_common.h"
 #include "tern_kernels.h"
 
 namespace tern {
 
 namespace {
 
-constexpr int SKIP_ROWS = 16;     // rows per workgroup of the zero-block skipping kernel
-constexpr int STEP = 1024;        // weights of one row per wave step
-constexpr int CHUNK = 64;         // weights per lane per row per step (16 bytes)
-constexpr int PIECES = 128;       // 16-byte activation pieces per (step, m): 16 chunks x 8
+using namespace gemv;
 
-// 16 code bytes that are read exactly once per product: a non-temporal load
-// (the weights stream through; nothing else reuses their cache lines).
-__device__ __forceinline__ uint4 load_codes(const uint8_t *p) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Sums of 2t*x over one lane's 64 weights (one 16-byte code vector) against
-// the pair-interleaved activation pieces xq[m][0..7] of the same chunk, for
-// every activation row m: each decoded pair feeds M packed dots.
-template <int M, bool BF16>
-__device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M][8], float (&part)[M]) {
-    const uint64_t a = sign_nz_fields64((uint64_t)code.x | ((uint64_t)code.y << 32));
-    const uint64_t b = sign_nz_fields64((uint64_t)code.z | ((uint64_t)code.w << 32));
-    auto step = [&](auto ic) {
-        constexpr int I = decltype(ic)::value;
-        constexpr int q = I >> 2;
-        constexpr int e = I & 3;
-        uint32_t p0, p1, p2, p3;
-        weight_pairs2<I>(a, p0, p1);   // words 0, 1
-        weight_pairs2<I>(b, p2, p3);   // words 2, 3
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            part[m] = dot2<BF16>(p0, (&xq[m][0 + q].x)[e], part[m]);
-            part[m] = dot2<BF16>(p1, (&xq[m][2 + q].x)[e], part[m]);
-            part[m] = dot2<BF16>(p2, (&xq[m][4 + q].x)[e], part[m]);
-            part[m] = dot2<BF16>(p3, (&xq[m][6 + q].x)[e], part[m]);
-        }
-    };
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    step(std::integral_constant<int, 3>{});
-    step(std::integral_constant<int, 4>{});
-    step(std::integral_constant<int, 5>{});
-    step(std::integral_constant<int, 6>{});
-    step(std::integral_constant<int, 7>{});
-}
-
-// S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N]
-// (the int8-scale variant) instead of fp16 values S[N,K/128].
-// JR: rows per 16-lane team; a workgroup covers ROWS = 4 JR rows.
 template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
@@ -230,189 +184,6 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
     }
 }
 
-// ---------------------------------------------------------------------------
-// Zero-block skipping (2kiu.com/news/5082861 §6 proposes skipping blocks that
-// are entirely zero to save bandwidth and compute).  MAP[n, w] bit b marks
-// block 32w + b of row n as holding a nonzero weight (tern_block_map).  The
-// work layout is the kernel above; per wave step, each 16-lane team (rows
-// n0 + 4j + r, j = 0..3, chunks kk = 0..15) lists the (row, chunk) pairs whose
-// block is marked, in (j, chunk) order, through a wave-private LDS slot, and
-// lane kk then takes items kk, kk+16, kk+32, kk+48 of the list.  Only listed
-// chunks load codes and scales, and a pass that no lane of the wave needs is
-// not executed: zero blocks cost neither bytes nor decode work.  Each lane
-// still accumulates per row j, so the reduction is the dense kernel's.
-template <int M, bool XBF16, int YT, int SPW>
-__global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const uint16_t *__restrict__ X,
-                                                                      const uint8_t *__restrict__ P,
-                                                                      const uint16_t *__restrict__ S,
-                                                                      const uint32_t *__restrict__ MAP,
-                                                                      void *__restrict__ Y, int N, int K) {
-    extern __shared__ uint4 lds[];
-    const int nsteps = (K + STEP - 1) / STEP;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int r = lane >> 4;
-    const int kk = lane & 15;
-    const int n0 = blockIdx.x * SKIP_ROWS;
-    const int64_t row_bytes = K >> 2;
-    const int groups = K >> 7;
-    const int mapw = (groups + 31) >> 5;
-    uint4 *xw = lds + wave * (SPW * M * PIECES);
-    float *red = reinterpret_cast<float *>(lds + nwaves * (SPW * M * PIECES));
-    uint8_t *slots = reinterpret_cast<uint8_t *>(red + nwaves * SKIP_ROWS * M) + wave * (SPW * 4 * 64);
-    const int s_begin = wave * SPW;
-    const int nchunks = K / CHUNK;
-
-    // ---- 1. activation loads and the map words of this wave's steps ----
-    uint4 xraw[SPW][M][2];
-    uint32_t mw[SPW][4];
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-        const int c = min((s_begin + si) * 16 + kk, nchunks - 1);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (int64_t)c * CHUNK + r * 16);
-            xraw[si][m][0] = src[0];
-            xraw[si][m][1] = src[1];
-        }
-        const int st = min(s_begin + si, nsteps - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mw[si][j] = MAP[(int64_t)min(n0 + 4 * j + r, N - 1) * mapw + (st >> 2)];
-    }
-
-    // ---- 2. stage the activations (as the dense kernel) ----
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            uint32_t pr[8];
-            interleave16(xraw[si][m][0], xraw[si][m][1], pr);
-            uint4 *dst = xw + (si * M + m) * PIECES;
-            dst[(2 * r) * 16 + kk] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-            dst[(2 * r + 1) * 16 + kk] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
-        }
-    }
-
-    // ---- 3. list each team's marked (row, chunk) pairs: item byte = 16 j + chunk ----
-    int count[SPW];
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-        const int st = s_begin + si;
-        const bool chunk_ok = st < nsteps && st * 16 + kk < nchunks;
-        int base = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool act = chunk_ok && n0 + 4 * j + r < N &&
-                             ((mw[si][j] >> (((st & 3) << 3) + (kk >> 1))) & 1u);
-            const uint32_t tb = (uint32_t)(__ballot(act) >> (16 * r)) & 0xFFFFu;
-            if (act) slots[(si * 4 + r) * 64 + base + __popc(tb & ((1u << kk) - 1u))] = (uint8_t)(16 * j + kk);
-            base += __popc(tb);
-        }
-        count[si] = base;
-    }
-    // activations and lists are private to this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- 4. codes and scales of the listed chunks only ----
-    uint4 code[SPW][4];
-    uint32_t sbits[SPW][4];
-    uint32_t item[SPW][4];
-    bool pass[SPW][4];
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool mine = kk + 16 * t < count[si];
-            pass[si][t] = __ballot(mine) != 0;   // uniform: does any lane of the wave need pass t?
-            item[si][t] = mine ? slots[(si * 4 + r) * 64 + kk + 16 * t] : 0u;
-            if (mine) {
-                const int j = item[si][t] >> 4;
-                const int c = (s_begin + si) * 16 + (item[si][t] & 15);
-                const int64_t n = n0 + 4 * j + r;
-                code[si][t] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
-                sbits[si][t] = S[n * groups + (c >> 1)];
-            }
-        }
-    }
-
-    // ---- 5. decode + accumulate the listed chunks into their rows ----
-    float acc[4][M];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
-#pragma unroll
-    for (int si = 0; si < SPW; ++si) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (!pass[si][t]) continue;
-            const bool mine = kk + 16 * t < count[si];
-            const int j = item[si][t] >> 4;
-            const int cl = item[si][t] & 15;
-            const float s = f16_bits_to_float((uint16_t)sbits[si][t]) * 0.5f;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                uint4 xq[1][8];
-                const uint4 *src = xw + (si * M + m) * PIECES;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) xq[0][q] = src[q * 16 + cl];
-                float part[1] = {0.f};
-                chunk_dot<1, XBF16>(code[si][t], xq, part);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    acc[jj][m] = (mine && j == jj) ? fmaf(s, part[0], acc[jj][m]) : acc[jj][m];
-                if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- 6. reduce as the dense kernel ----
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[j][m] = row16_sum(acc[j][m]);
-    if (kk == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int m = 0; m < M; ++m) red[(wave * SKIP_ROWS + 4 * j + r) * M + m] = acc[j][m];
-    }
-    __syncthreads();
-    if (tid < SKIP_ROWS * M) {
-        const int row = tid % SKIP_ROWS;
-        const int m = tid / SKIP_ROWS;
-        float y = 0.f;
-        for (int w = 0; w < nwaves; ++w) y += red[(w * SKIP_ROWS + row) * M + m];
-        const int n = n0 + row;
-        if (n < N) store_out<YT>(Y, (int64_t)m * N + n, y);
-    }
-}
-
-struct GemvShape {
-    int nsteps, spw, nwaves, jr;
-    size_t lds;
-};
-
-GemvShape gemv_shape(int64_t M, int64_t K) {
-    GemvShape g;
-    g.nsteps = (int)((K + STEP - 1) / STEP);
-    const int max_waves = M == 1 ? 16 : 8;  // (M > 1 needs the 256-register budget of <= 512 threads)
-    g.spw = (g.nsteps + max_waves - 1) / max_waves;
-    if (g.spw < 1) g.spw = 1;
-    g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
-    // rows per team: 2 (8-row workgroups); 1 when one row's K already gives
-    // every wave two steps (M = 1, K > 16384).  Measured on the decode shapes:
-    // fewer rows per workgroup spread the rows of a layer over more CUs.
-    g.jr = (M == 1 && g.spw >= 2) ? 1 : 2;
-    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * g.jr * M * sizeof(float);
-    return g;
-}
-
 template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
     constexpr int ROWS = 4 * JR;
@@ -471,82 +242,7 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
     return a.x_dtype == 1 ? launch_gemv_y<M, true, false>(a) : launch_gemv_y<M, false, false>(a);
 }
 
-// LDS of the skipping kernel: staged activations, its 16-row reduction
-// buffer and the per-wave item lists
-size_t skip_lds(const GemvShape &g, int64_t M) {
-    return (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * SKIP_ROWS * M * sizeof(float) +
-           (size_t)g.nwaves * g.spw * 4 * 64;
-}
-
-template <int M, bool XBF16, int YT, int SPW>
-hipError_t launch_skip_t(const GemmArgs &a, const uint32_t *map, const GemvShape &g) {
-    auto kern = gemv_skip_kernel<M, XBF16, YT, SPW>;
-    const size_t lds = skip_lds(g, M);
-    if (lds > 64 * 1024) {
-        static std::atomic<uint64_t> done_mask{0};
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        const uint64_t bit = 1ull << (dev & 63);
-        if (!(done_mask.load(std::memory_order_acquire) & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            if (e != hipSuccess) return e;
-            done_mask.fetch_or(bit, std::memory_order_acq_rel);
-        }
-    }
-    const dim3 grid((unsigned)((a.N + SKIP_ROWS - 1) / SKIP_ROWS));
-    const dim3 block((unsigned)(64 * g.nwaves));
-    hipLaunchKernelGGL(kern, grid, block, lds, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, map, a.Y,
-                       (int)a.N, (int)a.K);
-    return hipGetLastError();
-}
-
-template <int M, bool XBF16, int YT>
-hipError_t launch_skip_s(const GemmArgs &a, const uint32_t *map) {
-    const GemvShape g = gemv_shape(M, a.K);
-    if constexpr (M == 1) {
-        if (g.spw == 1) return launch_skip_t<M, XBF16, YT, 1>(a, map, g);
-        return launch_skip_t<M, XBF16, YT, 2>(a, map, g);
-    } else {
-        switch (g.spw) {
-        case 1: return launch_skip_t<M, XBF16, YT, 1>(a, map, g);
-        case 2: return launch_skip_t<M, XBF16, YT, 2>(a, map, g);
-        case 3: return launch_skip_t<M, XBF16, YT, 3>(a, map, g);
-        default: return launch_skip_t<M, XBF16, YT, 4>(a, map, g);
-        }
-    }
-}
-
-template <int M, bool XBF16>
-hipError_t launch_skip_y(const GemmArgs &a, const uint32_t *map) {
-    switch (a.y_dtype) {
-    case 0: return launch_skip_s<M, XBF16, 0>(a, map);
-    case 1: return launch_skip_s<M, XBF16, 1>(a, map);
-    default: return launch_skip_s<M, XBF16, 2>(a, map);
-    }
-}
-
-template <int M>
-hipError_t launch_skip_m(const GemmArgs &a, const uint32_t *map) {
-    return a.x_dtype == 1 ? launch_skip_y<M, true>(a, map) : launch_skip_y<M, false>(a, map);
-}
-
 }  // namespace
-
-size_t gemv_skip_lds_bytes(int64_t M, int64_t K) {
-    if (gemv_lds_bytes(M, K) == (size_t)-1) return (size_t)-1;
-    return skip_lds(gemv_shape(M, K), M);
-}
-
-hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map) {
-    switch (a.M) {
-    case 1: return launch_skip_m<1>(a, map);
-    case 2: return launch_skip_m<2>(a, map);
-    case 3: return launch_skip_m<3>(a, map);
-    default: return launch_skip_m<4>(a, map);
-    }
-}
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) {
     const GemvShape g = gemv_shape(M, K);

@@ -26,7 +26,7 @@ hipError_t launch_gemv(const GemmArgs &a);
 // LDS bytes the GEMV needs for this M, K (it stages X[M,K] on chip).
 size_t gemv_lds_bytes(int64_t M, int64_t K);
 
-// Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 4).
+// Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 2).
 hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map);
 size_t gemv_skip_lds_bytes(int64_t M, int64_t K);
 
