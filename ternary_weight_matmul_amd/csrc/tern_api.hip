@@ -50,6 +50,27 @@ tern_status check_matmul_args(const void *X, tern_dtype x_dtype, const uint8_t *
 
 tern_status from_hip(hipError_t e) { return e == hipSuccess ? TERN_OK : TERN_ERR_HIP; }
 
+// Kernel arguments of a validated product: fp16 scales S, or int8 codes Q with
+// row factors R (exactly one of the two is set).
+tern::GemmArgs make_args(const void *X, tern_dtype x_dtype, const uint8_t *W, const uint16_t *S, const int8_t *Q,
+                         const float *R, void *Y, tern_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+                         hipStream_t stream) {
+    tern::GemmArgs a;
+    a.X = X;
+    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
+    a.W = W;
+    a.S = S;
+    a.Q = Q;
+    a.R = R;
+    a.Y = Y;
+    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.stream = stream;
+    return a;
+}
+
 bool gemv_fits(int64_t M, int64_t K) {
     return M >= 1 && M <= TERN_GEMV_MAX_M && tern::gemv_lds_bytes(M, K) <= kGemvLdsLimit;
 }
@@ -107,19 +128,7 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
     if (M == 0 || N == 0) return TERN_OK;
     if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
 
-    tern::GemmArgs a;
-    a.X = X;
-    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
-    a.W = packed_W;
-    a.S = scales;
-    a.Q = nullptr;
-    a.R = nullptr;
-    a.Y = Y;
-    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.stream = stream;
+    const tern::GemmArgs a = make_args(X, x_dtype, packed_W, scales, nullptr, nullptr, Y, y_dtype, M, N, K, stream);
     const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
@@ -156,19 +165,8 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
     if (M == 0 || N == 0) return TERN_OK;
     if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
 
-    tern::GemmArgs a;
-    a.X = X;
-    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
-    a.W = packed_W;
-    a.S = nullptr;
-    a.Q = scales_q;
-    a.R = row_factor;
-    a.Y = Y;
-    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.stream = stream;
+    const tern::GemmArgs a =
+        make_args(X, x_dtype, packed_W, nullptr, scales_q, row_factor, Y, y_dtype, M, N, K, stream);
     const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
@@ -196,19 +194,7 @@ tern_status tern_matmul_blockmap(const void *X, tern_dtype x_dtype, const uint8_
                                        stream);
     if (N == 0) return TERN_OK;
 
-    tern::GemmArgs a;
-    a.X = X;
-    a.x_dtype = x_dtype == TERN_BF16 ? 1 : 0;
-    a.W = packed_W;
-    a.S = scales;
-    a.Q = nullptr;
-    a.R = nullptr;
-    a.Y = Y;
-    a.y_dtype = y_dtype == TERN_F16 ? 0 : (y_dtype == TERN_BF16 ? 1 : 2);
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.stream = stream;
+    const tern::GemmArgs a = make_args(X, x_dtype, packed_W, scales, nullptr, nullptr, Y, y_dtype, M, N, K, stream);
     return from_hip(tern::launch_gemv_skip(a, block_map));
 }
 

@@ -7,22 +7,23 @@
 // on chip, never re-read from memory in the inner loop (§4.2, §4.3); wide
 // vector loads of the packed bytes (§4.3, third version).
 //
-// Work layout (one workgroup = 4 JR output rows x all of K; JR = 1 or 2):
+// Work layout (one workgroup = 4 JR = 8 output rows x all of K):
 //   * a wave "step" covers 4 JR rows x 1024 weights: lane = 16*r + kk; for
 //     j < JR the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
 //     offset step*1024 + 64*kk, so every load instruction reads four
 //     256-byte contiguous row segments;
 //   * the waves of a workgroup (up to 16 for M = 1, 8 otherwise) split the K
-//     steps.  Each wave first issues all of its weight and scale loads, then
-//     stages the activations of its own steps into a wave-private LDS slice
+//     steps.  Each wave first issues all of its loads (activations, then
+//     weights and scales), stages the activations of its own steps into a
+//     wave-private LDS slice
 //     (pair-interleaved, see tern_device.h; the four lanes that share a
 //     64-weight chunk stage a quarter each), then decodes and accumulates as
 //     the loads land;
 //   * each lane keeps one fp32 partial per (row, m); it is summed over the
 //     16 lanes of its DPP row, then across the waves through LDS in a fixed
 //     order (deterministic; no atomics, no workspace).
-//   * small workgroups (8 rows, or 4 when K > 16384 at M = 1) spread a
-//     layer's rows over many CUs, so no CU runs much more than its share.
+//   * small workgroups (8 rows) spread a layer's rows over many CUs, so no
+//     CU runs much more than its share.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -37,7 +38,7 @@ namespace {
 
 using namespace gemv;
 
-template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
+template <int M, bool XBF16, int YT, int SPW, bool S8>
 __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
     constexpr int MC = 1;
 #pragma unroll
     for (int si = 0; si < SPW; ++si) {
-        const bool kact = (s_begin + si) * 16 + kk < nchunks;   // this lane's chunk lies inside K
+        const uint32_t kact = opaque_mask((s_begin + si) * 16 + kk < nchunks);   // this lane's chunk lies inside K
 #pragma unroll
         for (int mb = 0; mb < M; mb += MC) {
             uint4 xq[MC][8];
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
                                     : f16_bits_to_float((uint16_t)sbits[si][j])) * 0.5f;
 #pragma unroll
                 for (int m = 0; m < MC; ++m)
-                    acc[j][mb + m] = kact ? fmaf(s, part[m], acc[j][mb + m]) : acc[j][mb + m];
+                    acc[j][mb + m] = masked_fma(kact, s, part[m], acc[j][mb + m]);
                 if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);   // one row's pairs live at a time
             }
         }
@@ -184,11 +185,10 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
     }
 }
 
-template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
+template <int M, bool XBF16, int YT, int SPW, bool S8>
 hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
     constexpr int ROWS = 4 * JR;
-    if (g.jr != JR) return hipErrorInvalidValue;   // the LDS size was computed for g.jr
-    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8, JR>;
+    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8>;
     if (g.lds > 64 * 1024) {
         // raise the dynamic-LDS limit once per device (not a stream operation,
         // so it is kept out of any graph capture after the first call)
@@ -215,14 +215,14 @@ template <int M, bool XBF16, int YT, bool S8>
 hipError_t launch_gemv_s(const GemmArgs &a) {
     const GemvShape g = gemv_shape(M, a.K);
     if constexpr (M == 1) {   // gemv_lds_bytes admits at most two steps per wave for M = 1
-        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
-        return launch_gemv_t<M, XBF16, YT, 2, S8, 1>(a, g);
+        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
+        return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
     } else {
         switch (g.spw) {
-        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
-        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8, 2>(a, g);
-        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8, 2>(a, g);
-        default: return launch_gemv_t<M, XBF16, YT, 4, S8, 2>(a, g);
+        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
+        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
+        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8>(a, g);
+        default: return launch_gemv_t<M, XBF16, YT, 4, S8>(a, g);
         }
     }
 }

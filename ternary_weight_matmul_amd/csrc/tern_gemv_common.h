@@ -25,6 +25,23 @@ __device__ __forceinline__ uint4 load_codes(const uint8_t *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// All ones where c holds, else zero, hidden from the optimiser: a select on
+// it stays a bit select instead of becoming a branch (the compiler would move
+// the scale load into that branch, after the activation staging, which puts a
+// second memory round trip on the kernel's critical path).
+__device__ __forceinline__ uint32_t opaque_mask(bool c) {
+    uint32_t m = c ? ~0u : 0u;
+    asm("" : "+v"(m));
+    return m;
+}
+
+// fmaf(s, p, acc) where mask is all ones, acc where it is zero.
+__device__ __forceinline__ float masked_fma(uint32_t mask, float s, float p, float acc) {
+    const uint32_t r = __builtin_bit_cast(uint32_t, fmaf(s, p, acc));
+    const uint32_t a = __builtin_bit_cast(uint32_t, acc);
+    return __builtin_bit_cast(float, (r & mask) | (a & ~mask));
+}
+
 // Sums of 2t*x over one lane's 64 weights (one 16-byte code vector) against
 // the pair-interleaved activation pieces xq[m][0..7] of the same chunk, for
 // every activation row m: each decoded pair feeds M packed dots.
@@ -57,11 +74,17 @@ __device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M
     step(std::integral_constant<int, 7>{});
 }
 
-// S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N]
-// (the int8-scale variant) instead of fp16 values S[N,K/128].
-// JR: rows per 16-lane team; a workgroup covers ROWS = 4 JR rows.
+// Rows per 16-lane team of the dense decode kernel; a workgroup covers
+// 4 JR = 8 rows.  (Measured on the decode shapes once every load issues
+// before the activation staging: 4-row workgroups and 16-row workgroups were
+// both slower, the latter from uneven work per CU at N = 5120.)
+constexpr int JR = 2;
+
+// Launch shape of a decode-path product: K steps per wave (spw), waves per
+// workgroup and the dynamic LDS bytes (activation slices plus the cross-wave
+// reduction of the dense kernel).
 struct GemvShape {
-    int nsteps, spw, nwaves, jr;
+    int nsteps, spw, nwaves;
     size_t lds;
 };
 
@@ -72,11 +95,7 @@ inline GemvShape gemv_shape(int64_t M, int64_t K) {
     g.spw = (g.nsteps + max_waves - 1) / max_waves;
     if (g.spw < 1) g.spw = 1;
     g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
-    // rows per team: 2 (8-row workgroups); 1 when one row's K already gives
-    // every wave two steps (M = 1, K > 16384).  Measured on the decode shapes:
-    // fewer rows per workgroup spread the rows of a layer over more CUs.
-    g.jr = (M == 1 && g.spw >= 2) ? 1 : 2;
-    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * g.jr * M * sizeof(float);
+    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * JR * M * sizeof(float);
     return g;
 }
 

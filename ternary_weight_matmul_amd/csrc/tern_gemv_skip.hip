@@ -20,11 +20,9 @@ using namespace gemv;
 
 constexpr int SKIP_ROWS = 16;     // rows per workgroup of the zero-block skipping kernel
 
-// ---------------------------------------------------------------------------
-// Zero-block skipping (2kiu.com/news/5082861 §6 proposes skipping blocks that
-// are entirely zero to save bandwidth and compute).  MAP[n, w] bit b marks
-// block 32w + b of row n as holding a nonzero weight (tern_block_map).  The
-// work layout is the kernel above; per wave step, each 16-lane team (rows
+// MAP[n, w] bit b marks block 32w + b of row n as holding a nonzero weight
+// (tern_block_map).  The work layout is that of the dense decode kernel in
+// tern_gemv.hip; per wave step, each 16-lane team (rows
 // n0 + 4j + r, j = 0..3, chunks kk = 0..15) lists the (row, chunk) pairs whose
 // block is marked, in (j, chunk) order, through a wave-private LDS slot, and
 // lane kk then takes items kk, kk+16, kk+32, kk+48 of the list.  Only listed
