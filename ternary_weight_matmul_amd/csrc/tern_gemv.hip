@@ -7,7 +7,7 @@
 // on chip, never re-read from memory in the inner loop (§4.2, §4.3); wide
 // vector loads of the packed bytes (§4.3, third version).
 //
-// Work layout (one workgroup = 4 JR = 8 output rows x all of K):
+// Work layout (one workgroup = 4 JR output rows x all of K; JR = 2 or 3):
 //   * a wave "step" covers 4 JR rows x 1024 weights: lane = 16*r + kk; for
 //     j < JR the lane loads 16 bytes (64 weights) of row n0 + 4j + r at K
 //     offset step*1024 + 64*kk, so every load instruction reads four
@@ -22,8 +22,8 @@
 //   * each lane keeps one fp32 partial per (row, m); it is summed over the
 //     16 lanes of its DPP row, then across the waves through LDS in a fixed
 //     order (deterministic; no atomics, no workspace).
-//   * small workgroups (8 rows) spread a layer's rows over many CUs, so no
-//     CU runs much more than its share.
+//   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
+//     over many CUs, so no CU runs much more than its share.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -38,7 +38,7 @@ namespace {
 
 using namespace gemv;
 
-template <int M, bool XBF16, int YT, int SPW, bool S8>
+template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_t *__restrict__ X,
                                                      const uint8_t *__restrict__ P,
                                                      const uint16_t *__restrict__ S,
@@ -125,10 +125,12 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
 
-    // activation rows are taken one at a time (a row's 32 activation words in
-    // registers); for M > 1 each code word is decoded once per row, which
-    // keeps the register footprint of M = 1
-    constexpr int MC = 1;
+    // activation rows are taken MC at a time (a row's 32 activation words in
+    // registers); each code word is decoded once per group of MC rows.  Two
+    // rows per decode for even M (M = 2: 14-24% faster than one row at a
+    // time on the decode shapes), one for odd M, which keeps the register
+    // footprint of M = 1
+    constexpr int MC = M % 2 == 0 ? 2 : 1;
 #pragma unroll
     for (int si = 0; si < SPW; ++si) {
         const uint32_t kact = opaque_mask((s_begin + si) * 16 + kk < nchunks);   // this lane's chunk lies inside K
@@ -185,10 +187,11 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_kernel(const uint16_
     }
 }
 
-template <int M, bool XBF16, int YT, int SPW, bool S8>
+template <int M, bool XBF16, int YT, int SPW, bool S8, int JR>
 hipError_t launch_gemv_t(const GemmArgs &a, const GemvShape &g) {
     constexpr int ROWS = 4 * JR;
-    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8>;
+    if (g.jr != JR) return hipErrorInvalidValue;   // the LDS size was computed for g.jr
+    auto kern = gemv_kernel<M, XBF16, YT, SPW, S8, JR>;
     if (g.lds > 64 * 1024) {
         // raise the dynamic-LDS limit once per device (not a stream operation,
         // so it is kept out of any graph capture after the first call)
@@ -215,14 +218,14 @@ template <int M, bool XBF16, int YT, bool S8>
 hipError_t launch_gemv_s(const GemmArgs &a) {
     const GemvShape g = gemv_shape(M, a.K);
     if constexpr (M == 1) {   // gemv_lds_bytes admits at most two steps per wave for M = 1
-        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
-        return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
+        if (g.spw == 1) return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
+        return launch_gemv_t<M, XBF16, YT, 2, S8, 3>(a, g);
     } else {
         switch (g.spw) {
-        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8>(a, g);
-        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8>(a, g);
-        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8>(a, g);
-        default: return launch_gemv_t<M, XBF16, YT, 4, S8>(a, g);
+        case 1: return launch_gemv_t<M, XBF16, YT, 1, S8, 2>(a, g);
+        case 2: return launch_gemv_t<M, XBF16, YT, 2, S8, 3>(a, g);
+        case 3: return launch_gemv_t<M, XBF16, YT, 3, S8, 3>(a, g);
+        default: return launch_gemv_t<M, XBF16, YT, 4, S8, 3>(a, g);
         }
     }
 }

@@ -74,17 +74,12 @@ __device__ __forceinline__ void chunk_dot(const uint4 &code, const uint4 (&xq)[M
     step(std::integral_constant<int, 7>{});
 }
 
-// Rows per 16-lane team of the dense decode kernel; a workgroup covers
-// 4 JR = 8 rows.  (Measured on the decode shapes once every load issues
-// before the activation staging: 4-row workgroups and 16-row workgroups were
-// both slower, the latter from uneven work per CU at N = 5120.)
-constexpr int JR = 2;
-
 // Launch shape of a decode-path product: K steps per wave (spw), waves per
-// workgroup and the dynamic LDS bytes (activation slices plus the cross-wave
-// reduction of the dense kernel).
+// workgroup, rows per 16-lane team of the dense kernel (jr; its workgroups
+// cover 4 jr rows) and the dynamic LDS bytes (activation slices plus the
+// cross-wave reduction of the dense kernel).
 struct GemvShape {
-    int nsteps, spw, nwaves;
+    int nsteps, spw, nwaves, jr;
     size_t lds;
 };
 
@@ -95,7 +90,14 @@ inline GemvShape gemv_shape(int64_t M, int64_t K) {
     g.spw = (g.nsteps + max_waves - 1) / max_waves;
     if (g.spw < 1) g.spw = 1;
     g.nwaves = (g.nsteps + g.spw - 1) / g.spw;
-    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * JR * M * sizeof(float);
+    // rows per team: 2 (8-row workgroups); 3 when each wave takes two or more
+    // steps (K > 16384 at M = 1), where the activation slice every workgroup
+    // stages is large enough that sharing it over 12 rows pays for the less
+    // even spread of rows over the CUs.  Measured on the decode shapes, with
+    // every load issued before the activation staging: 4-row workgroups were
+    // slower everywhere, 16-row ones at N = 5120.
+    g.jr = g.spw >= 2 ? 3 : 2;
+    g.lds = (size_t)g.nwaves * g.spw * M * PIECES * 16 + (size_t)g.nwaves * 4 * g.jr * M * sizeof(float);
     return g;
 }
 
