@@ -17,11 +17,12 @@
 //   * LDS rows are 128 bytes with their eight 16-byte chunks XOR-swizzled by
 //     (row / 2) mod 8: the 16 lanes reading one MFMA fragment, and the lanes
 //     writing a row, touch 64 distinct banks;
-//   * both tiles are double-buffered, one barrier per step; an iteration
-//     writes step s+1 (held in registers) to LDS, issues the global loads of
-//     step s+2 and runs the MFMAs of step s, with no branches, so the decode
-//     can interleave with the MFMAs and each load has a step to land; each
-//     group of 8 lanes reads one 128-byte row segment of X (coalesced);
+//   * both tiles are double-buffered in LDS, one barrier per step; an
+//     iteration writes step s+1 (held in registers) to LDS, issues the global
+//     loads of step s+2 (or s+3, with two register sets of staged loads) and
+//     runs the MFMAs of step s, with no branches, so the decode can
+//     interleave with the MFMAs and each load has one step (two) to land;
+//     each group of 8 lanes reads one 128-byte row segment of X (coalesced);
 //   * v_mfma_f32_16x16x32_f16: lane l supplies A[l%16][8(l/16)+e] and
 //     B[8(l/16)+e][l%16], e = 0..7: one 16-byte chunk of an LDS row.
 // Workgroups are renumbered so that each XCD gets a contiguous run of tiles
@@ -45,7 +46,7 @@ constexpr int ROWB = 128;    // bytes per LDS row (KS fp16)
 // byte offset of 16-byte chunk c of row r inside a tile
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int WM, int WN, int MB, int NB, int YT>
+template <int WM, int WN, int MB, int NB, int SETS, int YT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *__restrict__ X,
                                                                  const uint8_t *__restrict__ P,
                                                                  const uint16_t *__restrict__ S,
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     static_assert(AP * NT == BM * 8 && AP >= 2 && AP <= 4, "two to four X chunks per thread (kept in scalars)");
     static_assert(RSTEP % 16 == 0, "swizzle must not depend on the chunk index");
     static_assert(2 * BN <= NT, "one thread per 32 decoded weights");
+    static_assert(SETS == 1 || SETS == 2, "one or two register sets of staged loads");
     // [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * A_TILE + 2 * W_TILE];
 
@@ -105,24 +107,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     const int w_dst2 = swz(wc_col, 4 * wc_h + 2);
     const int w_dst3 = swz(wc_col, 4 * wc_h + 3);
 
-    uint4 xa0, xa1, xa2, xa3;
-    uint2 wcode;
-    uint32_t sbits;
-    auto load = [&](int s) {
+    // staged global loads: one register set (A), or two (A, B) when SETS = 2,
+    // used alternately so that each load has two iterations to land; plain
+    // scalars rather than an array or struct, so that they stay in registers
+    uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+    uint2 wca, wcb;
+    uint32_t sba, sbb;
+    auto load_into = [&](uint4 &x0, uint4 &x1, uint4 &x2, uint4 &x3, uint2 &wc, uint32_t &sb, int s) {
         const int64_t o = (int64_t)s * KS;
-        xa0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
-        xa1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
-        if constexpr (AP > 2) xa2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
-        if constexpr (AP > 3) xa3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
-        wcode = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
-        sbits = s_src[s >> 1];
+        x0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
+        x1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
+        if constexpr (AP > 2) x2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
+        if constexpr (AP > 3) x3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
+        wc = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
+        sb = s_src[s >> 1];
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](const uint4 &x0, const uint4 &x1, const uint4 &x2, const uint4 &x3, int buf) {
         uint8_t *a_t = lds + buf * A_TILE + x_dst;
-        *reinterpret_cast<uint4 *>(a_t) = xa0;
-        *reinterpret_cast<uint4 *>(a_t + RSTEP * ROWB) = xa1;
-        if constexpr (AP > 2) *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = xa2;
-        if constexpr (AP > 3) *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = xa3;
+        *reinterpret_cast<uint4 *>(a_t) = x0;
+        *reinterpret_cast<uint4 *>(a_t + RSTEP * ROWB) = x1;
+        if constexpr (AP > 2) *reinterpret_cast<uint4 *>(a_t + 2 * RSTEP * ROWB) = x2;
+        if constexpr (AP > 3) *reinterpret_cast<uint4 *>(a_t + 3 * RSTEP * ROWB) = x3;
     };
     auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
         if (w_role) {
@@ -181,21 +186,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     };
 
-    load(0);
-    store_x(0);
-    store_w(0, wcode, sbits);
-    load(1);
+    constexpr int DIST = SETS + 1;   // steps between a load and the MFMAs that use it
+    load_into(xa0, xa1, xa2, xa3, wca, sba, 0);
+    store_x(xa0, xa1, xa2, xa3, 0);
+    store_w(0, wca, sba);
+    load_into(xa0, xa1, xa2, xa3, wca, sba, 1);
+    if constexpr (SETS == 2) load_into(xb0, xb1, xb2, xb3, wcb, sbb, min(2, nsteps - 1));
     __syncthreads();
-    // steps 0 .. nsteps-2: write step s+1 (loaded one iteration earlier) to
-    // the other buffer, issue the loads of step s+2 (the last ones repeat step
-    // nsteps-1: in bounds, unused), then decode step s+1's weights while the
-    // MFMAs of step s run: decode instructions are spread between the MFMAs
-    for (int s = 0; s < nsteps - 1; ++s) {
+    // iteration s (steps 0 .. nsteps-2): the set given holds step s+1; write it
+    // to the other LDS buffer, refill the set with step s+DIST (past the end
+    // it repeats step nsteps-1: in bounds, unused), then decode step s+1's
+    // weights while the MFMAs of step s run: decode instructions are spread
+    // between the MFMAs
+    auto iter = [&](int s, uint4 &x0, uint4 &x1, uint4 &x2, uint4 &x3, uint2 &wcr, uint32_t &sbr) {
         const int buf = s & 1;
-        store_x(buf ^ 1);
-        const uint2 wc = wcode;
-        const uint32_t sb = sbits;
-        load(min(s + 2, nsteps - 1));
+        store_x(x0, x1, x2, x3, buf ^ 1);
+        const uint2 wc = wcr;
+        const uint32_t sb = sbr;
+        load_into(x0, x1, x2, x3, wcr, sbr, min(s + DIST, nsteps - 1));
         // first half's fragments are read before the decode writes to LDS, so
         // its MFMAs do not wait for them
         read_frags(buf, f0);
@@ -214,7 +222,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         read_frags(buf, f1);
         mfmas();
         __syncthreads();
+    };
+    int s = 0;
+    if constexpr (SETS == 2) {
+        for (; s + 1 < nsteps - 1; s += 2) {
+            iter(s, xa0, xa1, xa2, xa3, wca, sba);
+            iter(s + 1, xb0, xb1, xb2, xb3, wcb, sbb);
+        }
     }
+    for (; s < nsteps - 1; ++s) iter(s, xa0, xa1, xa2, xa3, wca, sba);
     read_frags((nsteps - 1) & 1, f0);
     mfmas();
     read_frags((nsteps - 1) & 1, f1);
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         }
 }
 
-template <int WM, int WN, int MB, int NB>
+template <int WM, int WN, int MB, int NB, int SETS>
 struct Tile {
     static constexpr int BM = 16 * MB * WM, BN = 16 * NB * WN;
     static int64_t count(const GemmArgs &a) { return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
@@ -244,16 +260,18 @@ struct Tile {
         const int64_t tiles_n = (a.N + BN - 1) / BN;
         const int64_t tiles_m = (a.M + BM - 1) / BM;
         if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, YT>), dim3((unsigned)(tiles_n * tiles_m)),
+        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, SETS, YT>), dim3((unsigned)(tiles_n * tiles_m)),
                            dim3(64 * WM * WN), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y,
                            (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
         return hipGetLastError();
     }
 };
 
-using Tile256 = Tile<2, 4, 8, 4>;   // 256 x 256, 8 waves of 128 x 64, one workgroup per CU
-using Tile192 = Tile<2, 4, 6, 4>;   // 192 x 256, 8 waves of 96 x 64, one workgroup per CU
-using Tile64 = Tile<2, 2, 4, 2>;    // 128 x 64, 4 waves of 64 x 32, three workgroups per CU
+// Two load sets where the registers allow (the 256 x 256 tile would spill):
+// M=256, 5120 -> 7168 runs 20% faster with them, M=2048, 5120 -> 17408 5%.
+using Tile256 = Tile<2, 4, 8, 4, 1>;   // 256 x 256, 8 waves of 128 x 64, one workgroup per CU
+using Tile192 = Tile<2, 4, 6, 4, 2>;   // 192 x 256, 8 waves of 96 x 64, one workgroup per CU
+using Tile64 = Tile<2, 2, 4, 2, 2>;    // 128 x 64, 4 waves of 64 x 32, three workgroups per CU
 
 // Pick the tile with the least estimated time: rounds of resident workgroups
 // times the output area a CU covers per round, divided by the CU throughput
