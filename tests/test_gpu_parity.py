@@ -121,7 +121,10 @@ def test_sweep_matrices(shape_id):
 # shapes off the tile grid, dtypes, paths
 # ---------------------------------------------------------------------------
 
+# (M <= 4 with K > 8192: decode workgroups of 12 rows, two activation rows per
+# decode for even M)
 RAGGED = [(1, 128, 1), (1, 640, 33), (2, 1152, 50), (3, 384, 17), (4, 3200, 29), (1, 17408, 5),
+          (2, 9216, 37), (3, 17408, 21), (4, 12288, 45),
           (5, 256, 3), (17, 640, 100), (130, 384, 257), (129, 1152, 300), (64, 128, 512)]
 
 
@@ -176,7 +179,8 @@ def test_scales_near_fp16_max_and_negative(M, path, xd):
 # exact arithmetic: bit-exact against the oracle rounded to the output type
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16), (200, 1024, 80)])
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16), (200, 1024, 80),
+                                   (2, 2048, 24), (2, 9216, 24), (4, 10240, 16), (1, 17408, 12)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
 @pytest.mark.parametrize("yd", ["f32", "bf16", "f16"])
 def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
