@@ -316,15 +316,15 @@ hipError_t launch_y(const GemmArgs &a) {
 
 }  // namespace
 
-// fp16 X and fp16 scales with at least this many rows go to the LDS-staged
-// kernel of tern_gemm_big.hip, which shares each weight decode across the
-// rows of a large tile (its exact t*s operand needs an fp16 scale, so int8
-// scales stay here).
+// fp16 X with at least this many rows goes to the LDS-staged kernel of
+// tern_gemm_big.hip, which shares each weight decode across the rows of a
+// large tile.  Its operand is the exact fp16 product t*s (t*q for int8
+// scales), which needs fp16 activations beside it; bf16 X stays here.
 constexpr int64_t kBigMinM = 128;
 
 hipError_t launch_gemm(const GemmArgs &a) {
-    if (a.Q != nullptr) return a.x_dtype == 1 ? launch_y<true, true>(a) : launch_y<false, true>(a);
     if (a.x_dtype == 0 && a.M >= kBigMinM) return launch_gemm_big(a);
+    if (a.Q != nullptr) return a.x_dtype == 1 ? launch_y<true, true>(a) : launch_y<false, true>(a);
     return a.x_dtype == 1 ? launch_y<true, false>(a) : launch_y<false, false>(a);
 }
 

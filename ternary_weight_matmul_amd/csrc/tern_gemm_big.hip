@@ -46,10 +46,12 @@ constexpr int ROWB = 128;    // bytes per LDS row (KS fp16)
 // byte offset of 16-byte chunk c of row r inside a tile
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int WM, int WN, int MB, int NB, int SETS, int YT>
+template <int WM, int WN, int MB, int NB, int SETS, int YT, bool S8>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *__restrict__ X,
                                                                  const uint8_t *__restrict__ P,
                                                                  const uint16_t *__restrict__ S,
+                                                                 const int8_t *__restrict__ Q,
+                                                                 const float *__restrict__ R,
                                                                  void *__restrict__ Y, int M, int N, int K,
                                                                  int tiles_m, int tiles_n) {
     constexpr int NT = 64 * WM * WN;
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     const int wc_h = tid & 1;
     const int64_t wn_g = min(n0 + wc_col, N - 1);                           // clamped: never stored
     const uint8_t *w_src = P + wn_g * row_bytes + 8 * wc_h;
-    const uint16_t *s_src = S + wn_g * groups;
+    const uint16_t *s_src = S + wn_g * groups;   // (S8: Q + wn_g * groups)
+    const int8_t *q_src = Q + wn_g * groups;
     const int w_dst0 = swz(wc_col, 4 * wc_h + 0);
     const int w_dst1 = swz(wc_col, 4 * wc_h + 1);
     const int w_dst2 = swz(wc_col, 4 * wc_h + 2);
@@ -120,7 +123,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         if constexpr (AP > 2) x2 = *reinterpret_cast<const uint4 *>(x_src2 + o);
         if constexpr (AP > 3) x3 = *reinterpret_cast<const uint4 *>(x_src3 + o);
         wc = *reinterpret_cast<const uint2 *>(w_src + (int64_t)s * (KS / 4));
-        sb = s_src[s >> 1];
+        if constexpr (S8) sb = (uint32_t)(int32_t)q_src[s >> 1];
+        else sb = s_src[s >> 1];
     };
     auto store_x = [&](const uint4 &x0, const uint4 &x1, const uint4 &x2, const uint4 &x3, int buf) {
         uint8_t *a_t = lds + buf * A_TILE + x_dst;
@@ -132,7 +136,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
         if (w_role) {
             const uint64_t v = sign_nz_fields64((uint64_t)wc.x | ((uint64_t)wc.y << 32));
-            const uint32_t s2 = sb | (sb << 16);
+            // S8: the block's int8 code q as an fp16 value (exact: |q| <= 127);
+            // the row factor multiplies the finished sums in the epilogue
+            const uint32_t sh = S8 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int32_t)sb) : sb;
+            const uint32_t s2 = sh | (sh << 16);
             // products of weights (i, i+8) of code word 0 (a*) and word 1 (b*)
             uint32_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
             scaled_pairs2<0>(v, s2, a0, b0);
@@ -243,10 +250,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         for (int nb = 0; nb < NB; ++nb) {
             const int n = n0 + 16 * NB * wn + 16 * nb + li;
             if (n >= N) continue;
+            const float rowf = S8 ? R[n] : 1.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + 16 * MB * wm + 16 * mb + 4 * lg + i;
-                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, acc[mb][nb][i]);
+                if (m < M) store_out<YT>(Y, (int64_t)m * N + n, S8 ? acc[mb][nb][i] * rowf : acc[mb][nb][i]);
             }
         }
 }
@@ -255,13 +263,13 @@ template <int WM, int WN, int MB, int NB, int SETS>
 struct Tile {
     static constexpr int BM = 16 * MB * WM, BN = 16 * NB * WN;
     static int64_t count(const GemmArgs &a) { return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
-    template <int YT>
+    template <int YT, bool S8>
     static hipError_t launch(const GemmArgs &a) {
         const int64_t tiles_n = (a.N + BN - 1) / BN;
         const int64_t tiles_m = (a.M + BM - 1) / BM;
         if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, SETS, YT>), dim3((unsigned)(tiles_n * tiles_m)),
-                           dim3(64 * WM * WN), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Y,
+        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, SETS, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
+                           dim3(64 * WM * WN), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
                            (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
         return hipGetLastError();
     }
@@ -278,7 +286,7 @@ using Tile64 = Tile<2, 2, 4, 2, 2>;    // 128 x 64, 4 waves of 64 x 32, three wo
 // measured for that tile (1.0, 0.95, 0.55 relative; 256 CUs).  Quantisation
 // decides most shapes: e.g. 2048 x 17408 is 544 tiles of 256 x 256 (three
 // rounds, the last 71% idle) but 748 of 192 x 256 (three rounds, 97% full).
-template <int YT>
+template <int YT, bool S8>
 hipError_t launch_big_y(const GemmArgs &a) {
     constexpr int64_t kCUs = 256;
     auto cost = [&](int64_t tiles, int64_t area, int64_t per_cu, double thr) {
@@ -288,18 +296,19 @@ hipError_t launch_big_y(const GemmArgs &a) {
     const double c256 = cost(Tile256::count(a), 256 * 256, 1, 1.0);
     const double c192 = cost(Tile192::count(a), 192 * 256, 1, 0.95);
     const double c64 = cost(Tile64::count(a), 128 * 64, 3, 0.55);
-    if (c64 <= c256 && c64 <= c192) return Tile64::launch<YT>(a);
-    if (c192 < c256) return Tile192::launch<YT>(a);
-    return Tile256::launch<YT>(a);
+    if (c64 <= c256 && c64 <= c192) return Tile64::launch<YT, S8>(a);
+    if (c192 < c256) return Tile192::launch<YT, S8>(a);
+    return Tile256::launch<YT, S8>(a);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_big(const GemmArgs &a) {
+    const bool s8 = a.Q != nullptr;
     switch (a.y_dtype) {
-    case 0: return launch_big_y<0>(a);
-    case 1: return launch_big_y<1>(a);
-    default: return launch_big_y<2>(a);
+    case 0: return s8 ? launch_big_y<0, true>(a) : launch_big_y<0, false>(a);
+    case 1: return s8 ? launch_big_y<1, true>(a) : launch_big_y<1, false>(a);
+    default: return s8 ? launch_big_y<2, true>(a) : launch_big_y<2, false>(a);
     }
 }
 

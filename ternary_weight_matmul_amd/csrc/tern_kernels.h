@@ -35,8 +35,9 @@ hipError_t launch_block_map(const uint8_t *P, uint32_t *map, int64_t N, int64_t 
 
 // Batched path: MFMA GEMM, any M >= 1.
 hipError_t launch_gemm(const GemmArgs &a);
-// Batched path for many rows with fp16 X and fp16 scales: 256 x 256,
-// 192 x 256 or 128 x 64 tiles, weights decoded once per workgroup into LDS.
+// Batched path for many rows with fp16 X (fp16 scales, or int8 codes with
+// row factors): 256 x 256, 192 x 256 or 128 x 64 tiles, weights decoded once
+// per workgroup into LDS.
 hipError_t launch_gemm_big(const GemmArgs &a);
 
 // Int8 scale codes: Q[n,g] = rint(S[n,g] / R[n]), R[n] = max_g |S[n,g]| / 127.

@@ -57,7 +57,7 @@ def _run_s8(p, q, r, path):
 
 
 RAGGED = [(1, 128, 1), (1, 640, 33), (3, 1152, 50), (4, 3200, 29), (1, 17408, 5), (5, 256, 3),
-          (17, 640, 100), (130, 384, 257), (64, 128, 512)]
+          (17, 640, 100), (130, 384, 257), (64, 128, 512), (257, 640, 300), (1000, 256, 70)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
@@ -88,18 +88,21 @@ def test_matmul_s8_workloads(cfg, shape_id):
     check(y[ms, ns], p.y_dtype, Y, B, f"cfg{cfg}/{shape_id}")
 
 
-def test_matmul_s8_exact_bit_exact():
+@pytest.mark.parametrize("M,K,N,xd", [(3, 2048, 72, "bf16"), (200, 1024, 80, "f16"), (3, 2048, 72, "f16")])
+def test_matmul_s8_exact_bit_exact(M, K, N, xd):
     """Integer activations, power-of-two row factors: every product and sum is
-    exact in fp32, so the output equals the oracle rounded, bit for bit."""
-    M, K, N = 3, 2048, 72
-    rng = np.random.default_rng(99)
-    xbits = workloads.to_bf16_bits(rng.integers(-8, 9, (M, K)).astype(np.float64))
+    exact in fp32, so the output equals the oracle rounded, bit for bit.
+    (M=200 with fp16 activations takes the large-tile kernel.)"""
+    rng = np.random.default_rng(99 + M)
+    xi = rng.integers(-8, 9, (M, K)).astype(np.float64)
+    xbits = workloads.to_bf16_bits(xi) if xd == "bf16" else xi.astype(np.float16).view(np.uint16)
     P = O().pack(workloads.draw_ternary(5, N, K))
     q = rng.integers(-127, 128, (N, K // 128)).astype(np.int8)
     r = (2.0 ** rng.integers(-12, -6, N)).astype(np.float32)
-    Y, _ = O().matmul_s8(xbits, "bf16", P, q, r, M, N, K)
-    for path, yd in (("gemv", "f32"), ("mfma", "f32"), ("gemv", "bf16"), ("mfma", "bf16")):
-        y = tern.matmul_s8(bits_to_device(xbits, "bf16"), torch.from_numpy(P).to(device()),
+    Y, _ = O().matmul_s8(xbits, xd, P, q, r, M, N, K)
+    paths = (("gemv", "f32"), ("mfma", "f32"), ("gemv", "bf16"), ("mfma", "bf16"))
+    for path, yd in paths if M <= tern.GEMV_MAX_M else [pp for pp in paths if pp[0] == "mfma"]:
+        y = tern.matmul_s8(bits_to_device(xbits, xd), torch.from_numpy(P).to(device()),
                            torch.from_numpy(q).to(device()), torch.from_numpy(r).to(device()),
                            out_dtype=TORCH_DT[yd], path=path)
         got = O().decode(out_bits(y, yd), yd)
