@@ -319,9 +319,13 @@ def zero_block_skip(rate: float = 0.5):
     return res
 
 
-def decode_sweep(reps: int = 3):
+def decode_sweep(reps: int = 3, fused: bool = False):
     """One token through 48 layers x 7 projections at M=1 (q, k, v, o 5120->5120; gate, up
-    5120->17408; down 17408->5120): 336 launches over distinct weights captured in one graph."""
+    5120->17408; down 17408->5120): 336 launches over distinct weights captured in one graph.
+
+    fused=True stores the projections that read the same activations as one matrix, as
+    merged linear layers do (q|k|v: 5120->15360, gate|up: 5120->34816): the same weight
+    bytes per token in 4 launches per layer (192) instead of 7."""
     import torch
 
     import ternary_weight_matmul_amd as tern
@@ -332,25 +336,31 @@ def decode_sweep(reps: int = 3):
     gen = torch.Generator(device=dev)
     gen.manual_seed(6)
     xs = {k: torch.randn((1, k), generator=gen, device=dev).to(torch.bfloat16) for k in (5120, 17408)}
+    shapes = [(sh.K, sh.N) for sh in cfg.shapes]
+    if fused:
+        layer = [(5120, 3 * 5120), (5120, 5120), (5120, 2 * 17408), (17408, 5120)]
+        assert sorted(shapes[:7]) == sorted([(5120, 5120)] * 4 + [(5120, 17408)] * 2 + [(17408, 5120)])
+        shapes = layer * (len(shapes) // 7)
     mats = []
     packed_bytes = scale_bytes = 0
-    for sh in cfg.shapes:
-        w = workloads.draw_packed_device(gen, sh.N, sh.K, cfg.code_probs)
-        s = workloads.draw_scales_device(gen, sh.N, sh.K // 128, cfg.scale_lo, cfg.scale_hi)
-        y = torch.empty((1, sh.N), dtype=torch.bfloat16, device=dev)
-        mats.append((xs[sh.K], w, s, y))
+    for K, N in shapes:
+        w = workloads.draw_packed_device(gen, N, K, cfg.code_probs)
+        s = workloads.draw_scales_device(gen, N, K // 128, cfg.scale_lo, cfg.scale_hi)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        mats.append((xs[K], w, s, y))
         packed_bytes += w.numel()
         scale_bytes += s.numel() * 2
     n = len(mats)
     ms = _graph_time_ms(lambda i: tern.matmul_into(*mats[i % n]), n * reps, n) * n
     tok_s = 1e3 / ms
-    return {"workload": "decode sweep: 48 layers x 7 projections, M=1, bf16",
+    what = ("48 layers x (q|k|v, o, gate|up, down)" if fused else "48 layers x 7 projections")
+    return {"workload": f"decode sweep: {what}, M=1, bf16",
             "launches_per_token": n, "ms_per_token": round(ms, 4), "tokens_per_s": round(tok_s, 2),
             "packed_weight_bytes_per_token": int(packed_bytes), "scale_bytes_per_token": int(scale_bytes),
             "packed_GBps": round(packed_bytes / (ms / 1e3) / 1e9, 1),
             "alg_GBps": round((packed_bytes + scale_bytes) / (ms / 1e3) / 1e9, 1),
             "hbm_roofline_ms_per_token": round((packed_bytes + scale_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
-            "launch_floor_ms_per_token": "336 x ~1.5 us (see calibration)"}
+            "launch_floor_ms_per_token": f"{n} x ~1.5 us (see calibration)"}
 
 
 def main():
@@ -473,6 +483,7 @@ def main():
         torch.cuda.empty_cache()
         out["comparison_route"] = [comparison_route(args.config, args.shape), comparison_route(4, 3)]
         out["decode_sweep"] = decode_sweep()
+        out["decode_sweep_fused_layout"] = decode_sweep(fused=True)
         torch.cuda.empty_cache()
         out["int8_scales"] = int8_scale_variant()
         out["zero_block_skip"] = zero_block_skip()

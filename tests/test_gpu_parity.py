@@ -117,6 +117,14 @@ def test_sweep_matrices(shape_id):
     _full(workloads.make_problem(6, shape_id), "auto")
 
 
+@pytest.mark.parametrize("K,N", [(5120, 3 * 5120), (5120, 2 * 17408)])
+def test_sweep_fused_layout_matrices(K, N):
+    """The merged projections of the fused-layout decode sweep (q|k|v and
+    gate|up stored as one matrix), with the sweep's code and scale
+    distributions, compared element by element."""
+    _full(workloads.make_problem(6, 0, shape=workloads.Shape(1, K, N, "fused")), "auto")
+
+
 # ---------------------------------------------------------------------------
 # shapes off the tile grid, dtypes, paths
 # ---------------------------------------------------------------------------
