@@ -98,10 +98,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     const int niter = (nkb + WK - 1) / WK;
 
     // ---- activation tile: global -> registers (clamped addresses) ----
-    // Rows at or past M are neither loaded nor staged: their LDS rows hold
+    // Every load is issued unconditionally, at a clamped in-bounds address
+    // (rows past M read row M - 1 again; K blocks past the end read the last
+    // one).  A load under a condition would leave the compiler unable to
+    // count the loads in flight, and it would then wait for all of them,
+    // including the prefetch two iterations ahead, at the top of every
+    // iteration.  Rows at or past M are not staged: their LDS rows hold
     // stale values, which reach only output rows that are never stored (row
-    // i of an MFMA result depends on row i of A alone).  With few activation
-    // rows this cuts the staging work in proportion.
+    // i of an MFMA result depends on row i of A alone).
     uint4 a_reg[A_UNITS][2];
     auto load_a = [&](int it) {
 #pragma unroll
@@ -114,10 +118,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             const int kb = min(it * WK + w, nkb - 1);
             const int64_t m = min(m0 + row, M - 1);
             const uint4 *src = reinterpret_cast<const uint4 *>(X + m * K + (int64_t)kb * BK + blk * 16);
-            if (m0 + row < M) {
-                a_reg[u][0] = src[0];
-                a_reg[u][1] = src[1];
-            }
+            a_reg[u][0] = src[0];
+            a_reg[u][1] = src[1];
         }
     };
     auto store_a = [&](int buf) {
@@ -157,23 +159,24 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint2 w0[NB], w1[NB];
-    uint32_t s0[NB], s1[NB];    // fp16 scale bits, or the sign-extended int8 code
+    // weight loads of iterations it and it + 1: a ring of two sets, each
+    // reloaded (for it + 2) by the iteration that used it, so no register
+    // copy has to wait for a load in flight
+    uint2 wa[NB], wb[NB];
+    uint32_t sa[NB], sb[NB];    // fp16 scale bits, or the sign-extended int8 code
     float rowf[NB];             // S8: the row factor of this lane's column, applied in the epilogue
     if constexpr (S8) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) rowf[nb] = R[min(n0 + nb * 16 + li, N - 1)];
     }
     load_a(0);
-    load_w(0, w0, s0);
+    load_w(0, wa, sa);
     store_a(0);
-    if (niter > 1) {
-        load_a(1);
-        load_w(1, w1, s1);
-    }
+    load_a(1);            // clamped: iteration 1 need not exist
+    load_w(1, wb, sb);
     __syncthreads();
 
-    for (int it = 0; it < niter; ++it) {
+    auto iteration = [&](const int it, uint2 (&w0)[NB], uint32_t (&s0)[NB]) {
         const int buf = it & 1;
         if (it * WK + wk < nkb) {             // this wave's K block exists (uniform per wave)
             // decode: field transform of the lane's two code words per column block
@@ -232,17 +235,22 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
                 }
             }
         }
-        // next tile into the other buffer; loads two iterations ahead
+        // next tile into the other buffer; loads two iterations ahead, issued
+        // whether or not that iteration exists (clamped, see load_a)
         if (it + 1 < niter) store_a(buf ^ 1);
-        if (it + 2 < niter) load_a(it + 2);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            w0[nb] = w1[nb];
-            s0[nb] = s1[nb];
-        }
-        if (it + 2 < niter) load_w(it + 2, w1, s1);
+        load_a(it + 2);
+        load_w(it + 2, w0, s0);
         __syncthreads();
+    };
+    // both halves of the loop body run on every trip (a conditional second
+    // half would make the compiler assume, at the top of the loop, that the
+    // first half's loads were the last ones issued, and wait for them)
+    int it = 0;
+    for (; it + 1 < niter; it += 2) {
+        iteration(it, wa, sa);
+        iteration(it + 1, wb, sb);
     }
+    if (it < niter) iteration(it, wa, sa);
 
     // ---- waves that split K: sum their partial tiles through LDS ----
     if constexpr (WK > 1) {
