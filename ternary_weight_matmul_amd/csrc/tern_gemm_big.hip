@@ -25,6 +25,9 @@
 //     each group of 8 lanes reads one 128-byte row segment of X (coalesced);
 //   * v_mfma_f32_16x16x32_f16: lane l supplies A[l%16][8(l/16)+e] and
 //     B[8(l/16)+e][l%16], e = 0..7: one 16-byte chunk of an LDS row.
+// With fewer tiles than CUs, a workgroup holds two such groups of waves
+// (KG = 2), each over one half of K with its own LDS buffers; the second
+// group's accumulators are added to the first's through LDS at the end.
 // Workgroups are renumbered so that each XCD gets a contiguous run of tiles
 // (tile_n fastest): workgroups resident on one XCD share activation rows in
 // its L2.
@@ -46,15 +49,15 @@ constexpr int ROWB = 128;    // bytes per LDS row (KS fp16)
 // byte offset of 16-byte chunk c of row r inside a tile
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int WM, int WN, int MB, int NB, int SETS, int YT, bool S8>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *__restrict__ X,
+template <int WM, int WN, int MB, int NB, int SETS, int KG, int YT, bool S8>
+__global__ __launch_bounds__(64 * WM * WN * KG) void gemm_big_kernel(const uint16_t *__restrict__ X,
                                                                  const uint8_t *__restrict__ P,
                                                                  const uint16_t *__restrict__ S,
                                                                  const int8_t *__restrict__ Q,
                                                                  const float *__restrict__ R,
                                                                  void *__restrict__ Y, int M, int N, int K,
                                                                  int tiles_m, int tiles_n) {
-    constexpr int NT = 64 * WM * WN;
+    constexpr int NT = 64 * WM * WN;          // threads of one K group
     constexpr int BM = 16 * MB * WM;
     constexpr int BN = 16 * NB * WN;
     constexpr int A_TILE = BM * ROWB;
@@ -65,10 +68,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     static_assert(RSTEP % 16 == 0, "swizzle must not depend on the chunk index");
     static_assert(2 * BN <= NT, "one thread per 32 decoded weights");
     static_assert(SETS == 1 || SETS == 2, "one or two register sets of staged loads");
-    // [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * A_TILE + 2 * W_TILE];
+    static_assert(KG == 1 || KG == 2, "one or two K groups");
+    // per K group: [A buffer 0][A buffer 1][W buffer 0][W buffer 1]
+    constexpr int GROUP_LDS = 2 * A_TILE + 2 * W_TILE;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[KG * GROUP_LDS];
 
-    const int tid = threadIdx.x;
+    // KG = 2: two groups of WM x WN waves take the two halves of K, each with
+    // its own LDS buffers; their tiles are summed through LDS at the end
+    const int kg = KG == 1 ? 0 : (int)(threadIdx.x / NT);
+    const int tid = KG == 1 ? (int)threadIdx.x : (int)(threadIdx.x % NT);
+    uint8_t *const lds = lds_all + kg * GROUP_LDS;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / WN;
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     const int n0 = tile_n * BN;
     const int64_t row_bytes = K >> 2;
     const int groups = K >> 7;
-    const int nsteps = K / KS;      // >= 2: K is a positive multiple of 128
+    const int nsteps = K / KS / KG;  // steps of this K group (>= 2: the launcher requires K >= 128 KG)
+    const int s_base = kg * nsteps;  // its first step
 
     // X loader: chunk j of this thread is row RSTEP j + tid/8, chunk tid%8 of the step;
     // rows past M are clamped to M-1 (read, never stored)
@@ -117,6 +127,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     uint2 wca, wcb;
     uint32_t sba, sbb;
     auto load_into = [&](uint4 &x0, uint4 &x1, uint4 &x2, uint4 &x3, uint2 &wc, uint32_t &sb, int s) {
+        s += s_base;
         const int64_t o = (int64_t)s * KS;
         x0 = *reinterpret_cast<const uint4 *>(x_src0 + o);
         x1 = *reinterpret_cast<const uint4 *>(x_src1 + o);
@@ -243,6 +254,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
     read_frags((nsteps - 1) & 1, f1);
     mfmas();
 
+    if constexpr (KG == 2) {
+        // the second K group's tile goes through LDS (its buffers are free
+        // after this barrier) and the first group adds it in a fixed order
+        static_assert((size_t)NT * MB * NB * 4 * sizeof(float) <= (size_t)GROUP_LDS, "reduction buffer");
+        float *red = reinterpret_cast<float *>(lds_all + GROUP_LDS);
+        __syncthreads();
+        if (kg == 1) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[((mb * NB + nb) * 4 + i) * NT + tid] = acc[mb][nb][i];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][nb][i] += red[((mb * NB + nb) * 4 + i) * NT + tid];
+    }
+
     // epilogue: lane l holds rows 4(l/16)+i, column l%16 of each 16 x 16 block
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -259,7 +294,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(const uint16_t *
         }
 }
 
-template <int WM, int WN, int MB, int NB, int SETS>
+template <int WM, int WN, int MB, int NB, int SETS, int KG = 1>
 struct Tile {
     static constexpr int BM = 16 * MB * WM, BN = 16 * NB * WN;
     static int64_t count(const GemmArgs &a) { return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
@@ -268,8 +303,8 @@ struct Tile {
         const int64_t tiles_n = (a.N + BN - 1) / BN;
         const int64_t tiles_m = (a.M + BM - 1) / BM;
         if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, SETS, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
-                           dim3(64 * WM * WN), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
+        hipLaunchKernelGGL((gemm_big_kernel<WM, WN, MB, NB, SETS, KG, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
+                           dim3(64 * WM * WN * KG), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
                            (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
         return hipGetLastError();
     }
@@ -280,6 +315,7 @@ struct Tile {
 using Tile256 = Tile<2, 4, 8, 4, 1>;   // 256 x 256, 8 waves of 128 x 64, one workgroup per CU
 using Tile192 = Tile<2, 4, 6, 4, 2>;   // 192 x 256, 8 waves of 96 x 64, one workgroup per CU
 using Tile64 = Tile<2, 2, 4, 2, 2>;    // 128 x 64, 4 waves of 64 x 32, three workgroups per CU
+using Tile64K2 = Tile<2, 2, 4, 2, 2, 2>;  // the same tile with K split over two groups of 4 waves
 
 // Pick the tile with the least estimated time: rounds of resident workgroups
 // times the output area a CU covers per round, divided by the CU throughput
@@ -296,7 +332,15 @@ hipError_t launch_big_y(const GemmArgs &a) {
     const double c256 = cost(Tile256::count(a), 256 * 256, 1, 1.0);
     const double c192 = cost(Tile192::count(a), 192 * 256, 1, 0.95);
     const double c64 = cost(Tile64::count(a), 128 * 64, 3, 0.55);
-    if (c64 <= c256 && c64 <= c192) return Tile64::launch<YT, S8>(a);
+    if (c64 <= c256 && c64 <= c192) {
+        // fewer 128 x 64 tiles than CUs: each CU would run one 4-wave
+        // workgroup (one wave per SIMD); two K groups give it eight.
+        // M=256, 5120 -> 7168: 50.1 -> 40.0 us.  With more tiles than CUs
+        // the 96 KB of LDS per workgroup costs more than it gains (M=256,
+        // 5120 -> 17408: 87 -> 115 us), so those keep one group.
+        if (Tile64::count(a) <= kCUs && a.K >= 256) return Tile64K2::launch<YT, S8>(a);
+        return Tile64::launch<YT, S8>(a);
+    }
     if (c192 < c256) return Tile192::launch<YT, S8>(a);
     return Tile256::launch<YT, S8>(a);
 }
