@@ -181,9 +181,10 @@ tern_status tern_quantize_scales(const uint16_t *scales, int8_t *scales_q, float
  * 1 byte per 128 weights instead of 2), with §4.2 for everything else.
  * Arguments, layouts, paths and errors as tern_matmul_path, with the fp16
  * scales replaced by scales_q [N,K/128] int8 and row_factor [N] fp32
- * (4-byte aligned; NULL only when M, N or K is 0).  The MFMA path runs the
- * 64 x 256 / 16 x 64 kernels for every M.  Accuracy: the tern_matmul bound
- * with S[n,g] = scales_q[n,g] * row_factor[n].
+ * (4-byte aligned; NULL only when M, N or K is 0).  Each path runs the
+ * kernels of tern_matmul_path, reading the int8 codes in place of the fp16
+ * scales.  Accuracy: the tern_matmul bound with
+ * S[n,g] = scales_q[n,g] * row_factor[n].
  */
 tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *packed_W, const int8_t *scales_q,
                            const float *row_factor, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,

@@ -309,7 +309,12 @@ hipError_t launch_t(const GemmArgs &a) {
 
 template <bool XBF16, int YT, bool S8>
 hipError_t launch_shape(const GemmArgs &a) {
-    if (a.M <= 16) return launch_t<1, 2, 1, 8, XBF16, YT, S8>(a);        // 16 x 32 tiles, K split over 8 waves
+    // M <= 16: 16 x 32 tiles of two 16-column waves, K split over 8 waves
+    // each (16 waves).  Measured on the 5120 <-> 17408 decode shapes against
+    // one 32-column wave x 8 (the previous choice): M = 4 19.2 / 19.0 us
+    // against 19.7 / 19.9, M = 16 22.1 / 22.7 against 22.7 / 23.7; 64-column
+    // tiles, or K split over 2 or 4 waves, were 5-90% slower.
+    if (a.M <= 16) return launch_t<1, 1, 2, 8, XBF16, YT, S8>(a);
     else return launch_t<4, 4, 4, 1, XBF16, YT, S8>(a);                  // 64 x 256
 }
 
