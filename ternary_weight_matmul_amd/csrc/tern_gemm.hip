@@ -74,6 +74,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     constexpr int A_UNITS = (A_UNITS_TOTAL + NT - 1) / NT;
     constexpr int A_TILE = BM * LDS_ROW;                  // bytes of one K block's activations
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * WK * A_TILE];
+    // CT: the workgroup loads its code tile (BN rows x WK K blocks) together,
+    // 32 threads per row, each 8 bytes, so each row's WK*32 bytes are read as
+    // one contiguous run; the tile is staged in LDS (double-buffered beside
+    // the activations) and each wave reads its MFMA operand bytes from there.
+    // Without it, a load instruction reads 32 bytes from each of 16 rows.
+    constexpr bool CT = WK > 1 && NT == BN * 4 * WK;
+    constexpr int C_ROW = WK * 32 + 16;                   // staged code row: +16 bytes keeps 8-byte reads conflict-free
+    __shared__ __attribute__((aligned(16))) uint8_t c_lds[CT ? 2 * BN * C_ROW : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -141,13 +149,29 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         }
     };
 
-    // ---- weights: 8 code bytes + one scale per column block (clamped) ----
+    // ---- CT: the workgroup's code tile, thread t -> row t / (4 WK), 8-byte piece t % (4 WK) ----
+    const int c_row = tid / (4 * WK);
+    const int c_piece = tid - c_row * (4 * WK);
+    const uint8_t *c_src = P + (int64_t)min(tile_n * BN + c_row, N - 1) * row_bytes;   // clamped: never stored
+    uint2 c_reg = make_uint2(0u, 0u);
+    auto load_c = [&](int it) {
+        if constexpr (CT) {
+            // past the last K block: the row's last 8 bytes (in bounds, unused)
+            const int64_t o = min((int64_t)it * (WK * 32) + c_piece * 8, row_bytes - 8);
+            c_reg = *reinterpret_cast<const uint2 *>(c_src + o);
+        }
+    };
+    auto store_c = [&](int buf) {
+        if constexpr (CT) *reinterpret_cast<uint2 *>(c_lds + (buf * BN + c_row) * C_ROW + c_piece * 8) = c_reg;
+    };
+
+    // ---- weights: 8 code bytes (unless CT) + one scale per column block (clamped) ----
     auto load_w = [&](int it, uint2 (&w)[NB], uint32_t (&s)[NB]) {
         const int kb = min(it * WK + wk, nkb - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int64_t n = min(n0 + nb * 16 + li, N - 1);
-            w[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
+            if constexpr (!CT) w[nb] = *reinterpret_cast<const uint2 *>(P + n * row_bytes + (int64_t)kb * (BK / 4) + lg * 8);
             if constexpr (S8) s[nb] = (uint32_t)(int32_t)Q[n * groups + kb];
             else s[nb] = S[n * groups + kb];
         }
@@ -170,9 +194,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         for (int nb = 0; nb < NB; ++nb) rowf[nb] = R[min(n0 + nb * 16 + li, N - 1)];
     }
     load_a(0);
+    load_c(0);
     load_w(0, wa, sa);
     store_a(0);
+    store_c(0);
     load_a(1);            // clamped: iteration 1 need not exist
+    load_c(1);
     load_w(1, wb, sb);
     __syncthreads();
 
@@ -182,8 +209,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             // decode: field transform of the lane's two code words per column block
             uint64_t v[NB];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                v[nb] = sign_nz_fields64((uint64_t)w0[nb].x | ((uint64_t)w0[nb].y << 32));
+            for (int nb = 0; nb < NB; ++nb) {
+                uint2 wv = w0[nb];
+                if constexpr (CT)
+                    wv = *reinterpret_cast<const uint2 *>(c_lds + (buf * BN + 16 * (NB * wn + nb) + li) * C_ROW +
+                                                          wk * 32 + lg * 8);
+                v[nb] = sign_nz_fields64((uint64_t)wv.x | ((uint64_t)wv.y << 32));
+            }
 
             float4_t part[MB][NB];
 #pragma unroll
@@ -237,8 +269,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         }
         // next tile into the other buffer; loads two iterations ahead, issued
         // whether or not that iteration exists (clamped, see load_a)
-        if (it + 1 < niter) store_a(buf ^ 1);
+        if (it + 1 < niter) {
+            store_a(buf ^ 1);
+            store_c(buf ^ 1);
+        }
         load_a(it + 2);
+        load_c(it + 2);
         load_w(it + 2, w0, s0);
         __syncthreads();
     };
