@@ -59,8 +59,12 @@ __device__ __forceinline__ float4_t mfma16x16x32(const uint4 &a, const uint4 &b,
 }
 
 // S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N].
-template <int MB, int NB, int WN, int WK, bool XBF16, int YT, bool S8>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ X,
+// XR: activation rows of a tile that are loaded and staged (a power of two,
+// XR = BM or, with one 16-row block, 4 or 8 when M <= XR).  With XR < 16 the
+// tile needs less LDS, and registers are capped for 8 waves per SIMD, so
+// two 16-wave workgroups fit on a CU.
+template <int MB, int NB, int WN, int WK, int XR, bool XBF16, int YT, bool S8>
+__global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(const uint16_t *__restrict__ X,
                                                              const uint8_t *__restrict__ P,
                                                              const uint16_t *__restrict__ S,
                                                              const int8_t *__restrict__ Q,
@@ -70,9 +74,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     constexpr int BM = 16 * MB;
     constexpr int BN = 16 * NB * WN;
     constexpr int NT = 64 * WN * WK;
-    constexpr int A_UNITS_TOTAL = WK * BM * (BK / 16);   // 16-element units per iteration
+    static_assert(XR == BM || (MB == 1 && (XR == 4 || XR == 8)), "rows staged per tile");
+    constexpr int A_UNITS_TOTAL = WK * XR * (BK / 16);   // 16-element units per iteration
     constexpr int A_UNITS = (A_UNITS_TOTAL + NT - 1) / NT;
-    constexpr int A_TILE = BM * LDS_ROW;                  // bytes of one K block's activations
+    constexpr int A_TILE = XR * LDS_ROW;                  // bytes of one K block's activations
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * WK * A_TILE];
     // CT: the workgroup loads its code tile (BN rows x WK K blocks) together,
     // 32 threads per row, each 8 bytes, so each row's WK*32 bytes are read as
@@ -118,9 +123,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     auto load_a = [&](int it) {
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
-            const int b = min(tid + NT * u, A_UNITS_TOTAL - 1);
-            const int w = b / (BM * 8);              // which of the WK K blocks
-            const int rem = b - w * (BM * 8);
+            const int b = min(tid + NT * u, A_UNITS_TOTAL - 1);   // past the last unit: load it again
+            const int w = b / (XR * 8);              // which of the WK K blocks
+            const int rem = b - w * (XR * 8);
             const int row = rem >> 3;
             const int blk = rem & 7;
             const int kb = min(it * WK + w, nkb - 1);
@@ -134,10 +139,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int u = 0; u < A_UNITS; ++u) {
             const int b = tid + NT * u;
-            const int rowb = (b - (b / (BM * 8)) * (BM * 8)) >> 3;
+            const int rowb = (b - (b / (XR * 8)) * (XR * 8)) >> 3;
             if ((A_UNITS * NT == A_UNITS_TOTAL || b < A_UNITS_TOTAL) && m0 + rowb < M) {
-                const int w = b / (BM * 8);
-                const int rem = b - w * (BM * 8);
+                const int w = b / (XR * 8);
+                const int rem = b - w * (XR * 8);
                 const int row = rem >> 3;
                 const int blk = rem & 7;
                 uint32_t pr[8];
@@ -222,7 +227,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-            const uint8_t *a_base = a_lds + (buf * WK + wk) * A_TILE + li * LDS_ROW + lg * 64;
+            // rows past XR (only when M <= XR) read a staged row: they feed
+            // output rows that are never stored
+            const uint8_t *a_base = a_lds + (buf * WK + wk) * A_TILE + (li & (XR - 1)) * LDS_ROW + lg * 64;
 
             // k-steps H and H+2 use pairs 4H..4H+3 of word 0 and of word 1:
             // one 64-bit shift per pair index gives both (low and high half)
@@ -331,13 +338,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         }
 }
 
-template <int MB, int NB, int WN, int WK, bool XBF16, int YT, bool S8>
+template <int MB, int NB, int WN, int WK, int XR, bool XBF16, int YT, bool S8>
 hipError_t launch_t(const GemmArgs &a) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
     const int64_t tiles_m = (a.M + BM - 1) / BM;
     if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XBF16, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XR, XBF16, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
                        dim3(64 * WN * WK), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
                        (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
@@ -350,8 +357,16 @@ hipError_t launch_shape(const GemmArgs &a) {
     // one 32-column wave x 8 (the previous choice): M = 4 19.2 / 19.0 us
     // against 19.7 / 19.9, M = 16 22.1 / 22.7 against 22.7 / 23.7; 64-column
     // tiles, or K split over 2 or 4 waves, were 5-90% slower.
-    if (a.M <= 16) return launch_t<1, 1, 2, 8, XBF16, YT, S8>(a);
-    else return launch_t<4, 4, 4, 1, XBF16, YT, S8>(a);                  // 64 x 256
+    // M <= 8 with K <= 8192 (at most 8 iterations): only the 4 or 8 rows that
+    // exist are staged, and two workgroups share a CU, so one's pipeline
+    // fill overlaps the other's work.  Measured, FFN up (K=5120): M = 4
+    // 18.5 -> 16.1 us, M = 8 18.7 -> 16.6 us.  With longer K it was 3-4%
+    // slower (FFN down, K=17408: the register cap of two workgroups per CU
+    // spills three registers), so those keep one 16-row workgroup per CU.
+    if (a.M <= 4 && a.K <= 8192) return launch_t<1, 1, 2, 8, 4, XBF16, YT, S8>(a);
+    if (a.M <= 8 && a.K <= 8192) return launch_t<1, 1, 2, 8, 8, XBF16, YT, S8>(a);
+    if (a.M <= 16) return launch_t<1, 1, 2, 8, 16, XBF16, YT, S8>(a);
+    return launch_t<4, 4, 4, 1, 64, XBF16, YT, S8>(a);                   // 64 x 256
 }
 
 template <bool XBF16, bool S8>

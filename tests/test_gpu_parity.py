@@ -133,7 +133,9 @@ def test_sweep_fused_layout_matrices(K, N):
 # decode for even M)
 RAGGED = [(1, 128, 1), (1, 640, 33), (2, 1152, 50), (3, 384, 17), (4, 3200, 29), (1, 17408, 5),
           (2, 9216, 37), (3, 17408, 21), (4, 12288, 45),
-          (5, 256, 3), (17, 640, 100), (130, 384, 257), (129, 1152, 300), (64, 128, 512)]
+          (5, 256, 3), (17, 640, 100), (130, 384, 257), (129, 1152, 300), (64, 128, 512),
+          # small-M MFMA with 4 or 8 staged rows (K <= 8192) and with 16 (K > 8192)
+          (6, 4096, 33), (8, 1152, 70), (8, 9216, 40), (16, 8192, 19)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
@@ -188,7 +190,8 @@ def test_scales_near_fp16_max_and_negative(M, path, xd):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16), (200, 1024, 80),
-                                   (2, 2048, 24), (2, 9216, 24), (4, 10240, 16), (1, 17408, 12)])
+                                   (2, 2048, 24), (2, 9216, 24), (4, 10240, 16), (1, 17408, 12), (8, 3072, 48),
+                                   (16, 2048, 40)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
 @pytest.mark.parametrize("yd", ["f32", "bf16", "f16"])
 def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
@@ -253,7 +256,7 @@ def _reserved_to_zero(P):
     return out
 
 
-@pytest.mark.parametrize("M,path", [(1, "gemv"), (4, "gemv"), (1, "mfma"), (96, "mfma")])
+@pytest.mark.parametrize("M,path", [(1, "gemv"), (4, "gemv"), (1, "mfma"), (4, "mfma"), (8, "mfma"), (96, "mfma")])
 def test_invariants_exact(M, path):
     p = workloads.make_custom(300 + M, M, 2048, 200, x_dtype="bf16", y_dtype="f32",
                               probs=(0.3, 0.3, 0.3, 0.1))
