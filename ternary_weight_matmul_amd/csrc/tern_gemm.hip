@@ -45,7 +45,18 @@ typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;              // K per block (= one scale group)
-constexpr int LDS_ROW = 272;         // bytes per staged activation row (256 + 16 pad)
+// A staged activation row (one K block, 256 bytes) either is padded to 272
+// bytes (SWZ = false) or keeps 256 bytes with its 16-byte chunks XOR-swizzled
+// by the row (SWZ = true); either way the 16 rows one MFMA operand read
+// touches fall in distinct banks.  The swizzle saves the LDS that lets two
+// 16 x 32 workgroups share a CU; the 64 x 256 tile runs faster padded
+// (M=64, 5120 -> 17408: 70.6 against 77.3 us).
+template <bool SWZ>
+__device__ __forceinline__ int x_chunk(int row, int c) {
+    return SWZ ? row * 256 + ((c ^ (row & 15)) << 4) : row * 272 + c * 16;
+}
+// Staged code rows (256 bytes, 32 pieces of 8 bytes), swizzled the same way.
+__device__ __forceinline__ int c_piece_off(int row, int p) { return row * 256 + ((p ^ ((row & 15) << 1)) << 3); }
 
 template <bool BF16>
 __device__ __forceinline__ float4_t mfma16x16x32(const uint4 &a, const uint4 &b, float4_t c) {
@@ -60,11 +71,11 @@ __device__ __forceinline__ float4_t mfma16x16x32(const uint4 &a, const uint4 &b,
 
 // S8: scales are int8 codes Q[N,K/128] times a per-row fp32 factor R[N].
 // XR: activation rows of a tile that are loaded and staged (a power of two,
-// XR = BM or, with one 16-row block, 4 or 8 when M <= XR).  With XR < 16 the
-// tile needs less LDS, and registers are capped for 8 waves per SIMD, so
-// two 16-wave workgroups fit on a CU.
-template <int MB, int NB, int WN, int WK, int XR, bool XBF16, int YT, bool S8>
-__global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(const uint16_t *__restrict__ X,
+// XR = BM or, with one 16-row block, 4 or 8 when M <= XR).
+// TWO: registers are capped for 8 waves per SIMD, so that two 16-wave
+// workgroups fit on a CU (the LDS of a 16 x 32 tile is at most 80 KB).
+template <int MB, int NB, int WN, int WK, int XR, bool TWO, bool XBF16, int YT, bool S8>
+__global__ __launch_bounds__(64 * WN * WK, TWO ? 8 : 1) void gemm_kernel(const uint16_t *__restrict__ X,
                                                              const uint8_t *__restrict__ P,
                                                              const uint16_t *__restrict__ S,
                                                              const int8_t *__restrict__ Q,
@@ -77,16 +88,16 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
     static_assert(XR == BM || (MB == 1 && (XR == 4 || XR == 8)), "rows staged per tile");
     constexpr int A_UNITS_TOTAL = WK * XR * (BK / 16);   // 16-element units per iteration
     constexpr int A_UNITS = (A_UNITS_TOTAL + NT - 1) / NT;
-    constexpr int A_TILE = XR * LDS_ROW;                  // bytes of one K block's activations
+    constexpr bool SWZ = MB == 1;                         // 16-row tiles: swizzled, unpadded rows
+    constexpr int A_TILE = XR * (SWZ ? 256 : 272);        // bytes of one K block's activations
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * WK * A_TILE];
     // CT: the workgroup loads its code tile (BN rows x WK K blocks) together,
     // 32 threads per row, each 8 bytes, so each row's WK*32 bytes are read as
     // one contiguous run; the tile is staged in LDS (double-buffered beside
     // the activations) and each wave reads its MFMA operand bytes from there.
     // Without it, a load instruction reads 32 bytes from each of 16 rows.
-    constexpr bool CT = WK > 1 && NT == BN * 4 * WK;
-    constexpr int C_ROW = WK * 32 + 16;                   // staged code row: +16 bytes keeps 8-byte reads conflict-free
-    __shared__ __attribute__((aligned(16))) uint8_t c_lds[CT ? 2 * BN * C_ROW : 16];
+    constexpr bool CT = WK == 8 && NT == BN * 4 * WK;     // 256-byte code rows of 32 pieces
+    __shared__ __attribute__((aligned(16))) uint8_t c_lds[CT ? 2 * BN * 256 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,9 +158,9 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
                 const int blk = rem & 7;
                 uint32_t pr[8];
                 interleave16(a_reg[u][0], a_reg[u][1], pr);
-                uint4 *dst = reinterpret_cast<uint4 *>(a_lds + (buf * WK + w) * A_TILE + row * LDS_ROW + blk * 32);
-                dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-                dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+                uint8_t *dst = a_lds + (buf * WK + w) * A_TILE;
+                *reinterpret_cast<uint4 *>(dst + x_chunk<SWZ>(row, 2 * blk)) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                *reinterpret_cast<uint4 *>(dst + x_chunk<SWZ>(row, 2 * blk + 1)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
             }
         }
     };
@@ -167,7 +178,7 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
         }
     };
     auto store_c = [&](int buf) {
-        if constexpr (CT) *reinterpret_cast<uint2 *>(c_lds + (buf * BN + c_row) * C_ROW + c_piece * 8) = c_reg;
+        if constexpr (CT) *reinterpret_cast<uint2 *>(c_lds + buf * BN * 256 + c_piece_off(c_row, c_piece)) = c_reg;
     };
 
     // ---- weights: 8 code bytes (unless CT) + one scale per column block (clamped) ----
@@ -217,8 +228,8 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
             for (int nb = 0; nb < NB; ++nb) {
                 uint2 wv = w0[nb];
                 if constexpr (CT)
-                    wv = *reinterpret_cast<const uint2 *>(c_lds + (buf * BN + 16 * (NB * wn + nb) + li) * C_ROW +
-                                                          wk * 32 + lg * 8);
+                    wv = *reinterpret_cast<const uint2 *>(c_lds + buf * BN * 256 +
+                                                          c_piece_off(16 * (NB * wn + nb) + li, wk * 4 + lg));
                 v[nb] = sign_nz_fields64((uint64_t)wv.x | ((uint64_t)wv.y << 32));
             }
 
@@ -229,7 +240,8 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
                 for (int j = 0; j < NB; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
             // rows past XR (only when M <= XR) read a staged row: they feed
             // output rows that are never stored
-            const uint8_t *a_base = a_lds + (buf * WK + wk) * A_TILE + (li & (XR - 1)) * LDS_ROW + lg * 64;
+            const int arow0 = li & (XR - 1);
+            const uint8_t *a_tile = a_lds + (buf * WK + wk) * A_TILE;
 
             // k-steps H and H+2 use pairs 4H..4H+3 of word 0 and of word 1:
             // one 64-bit shift per pair index gives both (low and high half)
@@ -248,9 +260,10 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    const uint8_t *arow = a_base + mb * 16 * LDS_ROW;
-                    const uint4 al = *reinterpret_cast<const uint4 *>(arow + H * 16);         // k-step H
-                    const uint4 ah = *reinterpret_cast<const uint4 *>(arow + (H + 2) * 16);   // k-step H+2
+                    // this lane's 32 activations of the block: chunks 4 lg .. 4 lg + 3
+                    const int r = arow0 + 16 * mb;
+                    const uint4 al = *reinterpret_cast<const uint4 *>(a_tile + x_chunk<SWZ>(r, 4 * lg + H));       // k-step H
+                    const uint4 ah = *reinterpret_cast<const uint4 *>(a_tile + x_chunk<SWZ>(r, 4 * lg + H + 2));   // k-step H+2
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         part[mb][nb] = mfma16x16x32<XBF16>(al, blo[nb], part[mb][nb]);
@@ -338,13 +351,13 @@ __global__ __launch_bounds__(64 * WN * WK, XR < 16 ? 8 : 1) void gemm_kernel(con
         }
 }
 
-template <int MB, int NB, int WN, int WK, int XR, bool XBF16, int YT, bool S8>
+template <int MB, int NB, int WN, int WK, int XR, bool TWO, bool XBF16, int YT, bool S8>
 hipError_t launch_t(const GemmArgs &a) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
     const int64_t tiles_m = (a.M + BM - 1) / BM;
     if (tiles_n * tiles_m > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XR, XBF16, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WN, WK, XR, TWO, XBF16, YT, S8>), dim3((unsigned)(tiles_n * tiles_m)),
                        dim3(64 * WN * WK), 0, a.stream, static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y,
                        (int)a.M, (int)a.N, (int)a.K, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
@@ -357,16 +370,18 @@ hipError_t launch_shape(const GemmArgs &a) {
     // one 32-column wave x 8 (the previous choice): M = 4 19.2 / 19.0 us
     // against 19.7 / 19.9, M = 16 22.1 / 22.7 against 22.7 / 23.7; 64-column
     // tiles, or K split over 2 or 4 waves, were 5-90% slower.
-    // M <= 8 with K <= 8192 (at most 8 iterations): only the 4 or 8 rows that
-    // exist are staged, and two workgroups share a CU, so one's pipeline
-    // fill overlaps the other's work.  Measured, FFN up (K=5120): M = 4
-    // 18.5 -> 16.1 us, M = 8 18.7 -> 16.6 us.  With longer K it was 3-4%
-    // slower (FFN down, K=17408: the register cap of two workgroups per CU
-    // spills three registers), so those keep one 16-row workgroup per CU.
-    if (a.M <= 4 && a.K <= 8192) return launch_t<1, 1, 2, 8, 4, XBF16, YT, S8>(a);
-    if (a.M <= 8 && a.K <= 8192) return launch_t<1, 1, 2, 8, 8, XBF16, YT, S8>(a);
-    if (a.M <= 16) return launch_t<1, 1, 2, 8, 16, XBF16, YT, S8>(a);
-    return launch_t<4, 4, 4, 1, 64, XBF16, YT, S8>(a);                   // 64 x 256
+    // K <= 8192 (at most 8 iterations): two workgroups share a CU, so one's
+    // pipeline fill overlaps the other's work; with M <= 8 only the 4 or 8
+    // rows that exist are staged.  Measured, FFN up (K=5120): M = 4 18.5 ->
+    // 16.1 us, M = 8 18.7 -> 16.6 us, M = 16 20.0 -> 19.1 us.  With longer K
+    // it was 3-4% slower (FFN down, K=17408: the register cap of two
+    // workgroups per CU spills a few registers), so those keep one
+    // workgroup per CU.
+    if (a.M <= 4 && a.K <= 8192) return launch_t<1, 1, 2, 8, 4, true, XBF16, YT, S8>(a);
+    if (a.M <= 8 && a.K <= 8192) return launch_t<1, 1, 2, 8, 8, true, XBF16, YT, S8>(a);
+    if (a.M <= 16 && a.K <= 8192) return launch_t<1, 1, 2, 8, 16, true, XBF16, YT, S8>(a);
+    if (a.M <= 16) return launch_t<1, 1, 2, 8, 16, false, XBF16, YT, S8>(a);
+    return launch_t<4, 4, 4, 1, 64, false, XBF16, YT, S8>(a);            // 64 x 256
 }
 
 template <bool XBF16, bool S8>
