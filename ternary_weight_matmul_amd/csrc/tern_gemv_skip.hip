@@ -92,8 +92,10 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const ui
         int base = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bool act = chunk_ok && n0 + 4 * j + r < N &&
-                             ((mw[si][j] >> (((st & 3) << 3) + (kk >> 1))) & 1u);
+            // a bit operation on an opaque mask: a short-circuit condition let
+            // the compiler move the map load into a branch, behind the staging
+            const uint32_t ok = opaque_mask(chunk_ok && n0 + 4 * j + r < N);
+            const bool act = ((mw[si][j] >> (((st & 3) << 3) + (kk >> 1))) & ok & 1u) != 0u;
             const uint32_t tb = (uint32_t)(__ballot(act) >> (16 * r)) & 0xFFFFu;
             if (act) slots[(si * 4 + r) * 64 + base + __popc(tb & ((1u << kk) - 1u))] = (uint8_t)(16 * j + kk);
             base += __popc(tb);
@@ -106,6 +108,11 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const ui
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- 4. codes and scales of the listed chunks only ----
+    // Every lane issues its loads of every pass: a lane without an item reads
+    // the first bytes of P and S instead, one cache line the whole GPU
+    // shares, so it adds no HBM traffic.  (Loads under a per-lane condition
+    // made the compiler wait for each pass's loads before issuing the next
+    // pass's: one memory round trip per pass.)
     uint4 code[SPW][4];
     uint32_t sbits[SPW][4];
     uint32_t item[SPW][4];
@@ -117,13 +124,13 @@ __global__ __launch_bounds__(M == 1 ? 1024 : 512) void gemv_skip_kernel(const ui
             const bool mine = kk + 16 * t < count[si];
             pass[si][t] = __ballot(mine) != 0;   // uniform: does any lane of the wave need pass t?
             item[si][t] = mine ? slots[(si * 4 + r) * 64 + kk + 16 * t] : 0u;
-            if (mine) {
-                const int j = item[si][t] >> 4;
-                const int c = (s_begin + si) * 16 + (item[si][t] & 15);
-                const int64_t n = n0 + 4 * j + r;
-                code[si][t] = *reinterpret_cast<const uint4 *>(P + n * row_bytes + (int64_t)c * 16);
-                sbits[si][t] = S[n * groups + (c >> 1)];
-            }
+            const int j = item[si][t] >> 4;
+            const int c = (s_begin + si) * 16 + (item[si][t] & 15);
+            const int64_t n = n0 + 4 * j + r;
+            const uint8_t *pa = mine ? P + n * row_bytes + (int64_t)c * 16 : P;
+            const uint16_t *sa = mine ? S + n * groups + (c >> 1) : S;
+            code[si][t] = *reinterpret_cast<const uint4 *>(pa);
+            sbits[si][t] = *sa;
         }
     }
 
