@@ -13,19 +13,28 @@
 // the waves' partial tiles are summed through LDS at the end (fixed order).
 // Per iteration:
 //   * X[rows, WK K blocks] goes global -> registers -> LDS, pair-interleaved
-//     (tern_device.h), 272-byte padded rows (16-byte reads without bank
-//     conflicts); the LDS tile is double-buffered (one barrier per iteration)
-//     and the global loads run two iterations ahead;
-//   * each lane loads 8 code bytes (32 weights) of its column for each of its
-//     NB column blocks (prefetched two iterations ahead) and decodes them in
-//     registers straight into MFMA B operands: +-2 pairs (tern_device.h),
-//     exact in fp16 and bf16; the block's fp32 partial sum is then scaled by
-//     s/2 in fp32 (the pages' scale-at-the-block-boundary step), so no scale
-//     is ever rounded or overflowed into the 16-bit operand;
+//     (tern_device.h); the LDS tile is double-buffered (one barrier per
+//     iteration) and the global loads run two iterations ahead.  16-row
+//     tiles stage only the XR rows that can exist (4, 8 or 16);
+//   * codes: in the 16 x 32 tiles (WK = 8) the workgroup loads the tile's
+//     code bytes together, 32 threads per row, so each row's 256 bytes of
+//     the iteration are one contiguous run, and stages them in LDS beside
+//     the activations; in the 64 x 256 tiles each lane loads the 8 code
+//     bytes (32 weights) of its column per column block, prefetched two
+//     iterations ahead in a ring of two register sets;
+//   * each lane decodes its 8 code bytes per column block straight into
+//     MFMA B operands: +-2 pairs (tern_device.h), exact in fp16 and bf16;
+//     the block's fp32 partial sum is then scaled by s/2 in fp32 (the pages'
+//     scale-at-the-block-boundary step), so no scale is ever rounded or
+//     overflowed into the 16-bit operand;
 //   * v_mfma_f32_16x16x32_{f16,bf16}: lane l gives A[l%16][8(l/16)+e] and
 //     B[8(l/16)+e][l%16]; the lane's 32 weights of a block are spread over the
 //     4 MFMA k-steps so that the activation fragment of step t is the 16-byte
-//     run X'[32g + 8t .. +8] of the pair-interleaved row.
+//     run X'[32g + 8t .. +8] of the pair-interleaved row;
+//   * every global load is issued unconditionally, at a clamped in-bounds
+//     address, so the compiler can count the loads in flight.
+// Staged rows are padded (64 x 256 tiles) or XOR-swizzled (16-row tiles, see
+// x_chunk) so the fragment reads are free of bank conflicts.
 // Workgroups are numbered so that each XCD (workgroups go round-robin over
 // the 8 XCDs) gets a contiguous run of tiles, which share activation rows in
 // that XCD's L2.
