@@ -316,6 +316,7 @@ using Tile256 = Tile<2, 4, 8, 4, 1>;   // 256 x 256, 8 waves of 128 x 64, one wo
 using Tile192 = Tile<2, 4, 6, 4, 2>;   // 192 x 256, 8 waves of 96 x 64, one workgroup per CU
 using Tile64 = Tile<2, 2, 4, 2, 2>;    // 128 x 64, 4 waves of 64 x 32, three workgroups per CU
 using Tile64K2 = Tile<2, 2, 4, 2, 2, 2>;  // the same tile with K split over two groups of 4 waves
+using Tile128K2 = Tile<2, 2, 4, 4, 2, 2>; // 128 x 128, two groups of 4 waves of 64 x 64 splitting K
 
 // Pick the tile with the least estimated time: rounds of resident workgroups
 // times the output area a CU covers per round, divided by the CU throughput
@@ -324,6 +325,7 @@ using Tile64K2 = Tile<2, 2, 4, 2, 2, 2>;  // the same tile with K split over two
 // rounds, the last 71% idle) but 748 of 192 x 256 (three rounds, 97% full).
 template <int YT, bool S8>
 hipError_t launch_big_y(const GemmArgs &a) {
+
     constexpr int64_t kCUs = 256;
     auto cost = [&](int64_t tiles, int64_t area, int64_t per_cu, double thr) {
         const int64_t rounds = (tiles + kCUs * per_cu - 1) / (kCUs * per_cu);
@@ -339,6 +341,13 @@ hipError_t launch_big_y(const GemmArgs &a) {
         // the 96 KB of LDS per workgroup costs more than it gains (M=256,
         // 5120 -> 17408: 87 -> 115 us), so those keep one group.
         if (Tile64::count(a) <= kCUs && a.K >= 256) return Tile64K2::launch<YT, S8>(a);
+        // more 128 x 64 tiles than CUs, but 128 x 128 tiles fill 3/4 to all
+        // of the CUs in one round: those, with two K groups (one 8-wave
+        // workgroup per CU).  M=4096, 1024 -> 1024: 19.4 -> 17.3 us; 3072 ->
+        // 1024: 46.2 -> 38.1 us.  Elsewhere they lost (e.g. 1024 -> 3072,
+        // 768 tiles: 36.1 -> 45.5 us).
+        const int64_t t128 = Tile128K2::count(a);
+        if (t128 <= kCUs && 4 * t128 >= 3 * kCUs && a.K >= 256) return Tile128K2::launch<YT, S8>(a);
         return Tile64::launch<YT, S8>(a);
     }
     if (c192 < c256) return Tile192::launch<YT, S8>(a);

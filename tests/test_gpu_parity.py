@@ -213,19 +213,22 @@ def test_exact_arithmetic_bit_exact(M, K, N, xd, yd):
         assert np.array_equal(got, want), (path, np.argwhere(got != want)[:5])
 
 
-@pytest.mark.parametrize("M,K,N,yd", [(2000, 256, 6000, "f16"), (1999, 384, 6001, "f32"), (1000, 128, 17000, "f32")])
+@pytest.mark.parametrize("M,K,N,yd", [(2000, 256, 6000, "f16"), (1999, 384, 6001, "f32"), (1000, 128, 17000, "f32"),
+                                      (3000, 384, 1100, "f16"), (200, 512, 3000, "f32")])
 def test_large_tiles_ragged(M, K, N, yd):
-    """Shapes that take the 256 x 256 tiles (the first two) and the 192 x 256
-    tiles (the last) with ragged row and column tails, compared element by
-    element."""
+    """Shapes that take the 256 x 256 tiles (the first two), the 192 x 256
+    tiles (the third), 128 x 128 tiles with two K groups (the fourth) and
+    128 x 64 tiles with two K groups (the last), with ragged row and column
+    tails, compared element by element."""
     p = workloads.make_custom(M + N, M, K, N, x_dtype="f16", y_dtype=yd, reserved_rate=0.02)
     _full(p, "auto")
 
 
-def test_large_tiles_exact_bit_exact():
-    """Exact arithmetic on the 256 x 256 tiles: bit-identical to the oracle."""
-    M, K, N = 2000, 256, 6000
-    rng = np.random.default_rng(4242)
+@pytest.mark.parametrize("M,K,N", [(2000, 256, 6000), (3000, 384, 1100)])
+def test_large_tiles_exact_bit_exact(M, K, N):
+    """Exact arithmetic on the 256 x 256 tiles and on the 128 x 128 tiles with
+    two K groups: bit-identical to the oracle."""
+    rng = np.random.default_rng(4242 + M)
     xbits = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
     P = O().pack(workloads.draw_ternary(77, N, K))
     sbits = (2.0 ** rng.integers(-4, 1, (N, K // 128))).astype(np.float16).view(np.uint16)
