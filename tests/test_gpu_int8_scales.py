@@ -57,7 +57,9 @@ def _run_s8(p, q, r, path):
 
 
 RAGGED = [(1, 128, 1), (1, 640, 33), (3, 1152, 50), (4, 3200, 29), (1, 17408, 5), (5, 256, 3),
-          (17, 640, 100), (130, 384, 257), (64, 128, 512), (257, 640, 300), (1000, 256, 70)]
+          (17, 640, 100), (130, 384, 257), (64, 128, 512), (257, 640, 300), (1000, 256, 70),
+          # small-M MFMA with 8 and 16 staged rows; with fp16 X, 128 x 128 tiles of two K groups
+          (8, 4096, 200), (16, 2048, 300), (3000, 384, 1100)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
