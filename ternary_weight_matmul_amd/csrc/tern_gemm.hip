@@ -386,10 +386,13 @@ hipError_t launch_shape(const GemmArgs &a) {
     // it was 3-4% slower (FFN down, K=17408: the register cap of two
     // workgroups per CU spills a few registers), so those keep one
     // workgroup per CU.
-    // M <= 4: 16-column workgroups of 8 waves (twice as many, four per CU):
-    // FFN up 16.0 -> 15.0 us, 5120 -> 5120 7.6 -> 7.3 us; at M = 8 no
-    // change, at M = 16 slower (the register cap is not met there).
+    // M <= 4: 16-column workgroups of 8 waves (twice as many; four per CU
+    // with the register cap at K <= 8192, two without it beyond): FFN up
+    // 16.0 -> 15.0 us, 5120 -> 5120 7.6 -> 7.3 us, FFN down 16.6 -> 16.1 us,
+    // 12288 -> 4096 13.7 -> 10.8 us.  At M = 8 no change or slower, at
+    // M = 16 slower.
     if (a.M <= 4 && a.K <= 8192) return launch_t<1, 1, 1, 8, 4, true, XBF16, YT, S8>(a);
+    if (a.M <= 4) return launch_t<1, 1, 1, 8, 4, false, XBF16, YT, S8>(a);
     if (a.M <= 8 && a.K <= 8192) return launch_t<1, 1, 2, 8, 8, true, XBF16, YT, S8>(a);
     if (a.M <= 16 && a.K <= 8192) return launch_t<1, 1, 2, 8, 16, true, XBF16, YT, S8>(a);
     if (a.M <= 16) return launch_t<1, 1, 2, 8, 16, false, XBF16, YT, S8>(a);
