@@ -157,6 +157,21 @@ def test_decode_rows_beyond_one_round(K, N, xd, yd):
         _full(p, path)
 
 
+@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 36864, 70, "bf16", "bf16"), (2, 40960, 45, "f16", "f32"),
+                                         (1, 65536, 9, "f16", "f16")])
+def test_decode_beyond_gemv_reach(M, K, N, xd, yd):
+    """K too long for the decode kernel's register budget (more than two
+    1024-weight steps per wave at M = 1, more than four at M = 2): the
+    automatic choice takes the MFMA kernel, and asking for the decode kernel
+    is refused before anything is launched."""
+    p = workloads.make_custom(M + K + N, M, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.01)
+    _full(p, "auto")
+    _full(p, "mfma")
+    with pytest.raises(tern.TernError) as err:
+        run(p, "gemv")
+    assert err.value.status == 6   # TERN_ERR_UNSUPPORTED
+
+
 def test_outliers_and_wide_scales():
     # activations with x20 outliers, scales spread over two decades
     p = workloads.make_custom(77, 8, 1024, 96, x_dtype="f16", y_dtype="f32", scale_lo=1e-3, scale_hi=4.0)
