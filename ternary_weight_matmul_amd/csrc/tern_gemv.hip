@@ -24,6 +24,9 @@
 //     order (deterministic; no atomics, no workspace).
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
+// A short-step variant (gemv_short_kernel, below) serves M = 1 with fp16
+// scales when K and N are at most 5120: one workgroup per CU at most,
+// 512-weight steps and 8 code bytes per lane and row.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -245,6 +248,156 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
     return a.x_dtype == 1 ? launch_gemv_y<M, true, false>(a) : launch_gemv_y<M, false, false>(a);
 }
 
+
+// ---- short-step variant: M = 1, fp16 scales, K <= 5120, N <= 5120 ----
+// The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
+// with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
+// CU gets the same share (8-row workgroups would leave half of the CUs with
+// one workgroup more than the others).  Each wave takes one 512-weight step,
+// so a workgroup has ceil(K / 512) <= 10 waves, and lane (r, kk) reads the
+// 8 code bytes (32 weights) of chunk kk of rows n0 + 4j + r.  The step's
+// activations (32 blocks of 16) are staged pair-interleaved in the wave's
+// LDS slice by lanes r = 0, 1; lanes r = 2, 3 write the same words again.
+// Measured at M = 1, bf16 (graph-timed, weights rotated), against the kernel
+// above: 5120 -> 5120 3.98 -> 3.94 us (4.22 -> 4.07 with bench.py's 2 GB
+// of rotated weights), 5120 -> 3072 3.58 -> 3.32, 2048 -> 5120 3.01 -> 2.88;
+// at K = 8192 or N = 6144 it was no better or slower.
+constexpr int SHORT_STEP = 512;   // weights of one row per wave
+constexpr int SHORT_CHUNK = 32;   // weights per lane per row (8 bytes)
+constexpr int SHORT_PIECES = 64;  // 16-byte activation pieces per step
+constexpr int64_t kShortMaxK = 5120;
+constexpr int64_t kShortMaxN = 5120;
+
+template <bool XBF16, int YT, int JR>
+__global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_kernel(
+    const uint16_t *__restrict__ X, const uint8_t *__restrict__ P, const uint16_t *__restrict__ S,
+    void *__restrict__ Y, int N, int K) {
+    constexpr int ROWS = 4 * JR;
+    extern __shared__ uint4 lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int r = lane >> 4;
+    const int kk = lane & 15;
+    const int n0 = blockIdx.x * ROWS;
+    const int64_t row_bytes = K >> 2;
+    const int groups = K >> 7;
+    const int nchunks = K / SHORT_CHUNK;
+    uint4 *xw = lds + wave * SHORT_PIECES;
+    float *red = reinterpret_cast<float *>(lds + nwaves * SHORT_PIECES);
+
+    // ---- 1. loads, all unconditional at clamped in-bounds addresses: the
+    //         activation block this lane stages first, then codes and scales
+    //         (the scheduling barriers keep that order, so the staging waits
+    //         for the activations alone) ----
+    const int blk = 2 * kk + (r & 1);   // 16-element block of this step
+    const uint4 *xs = reinterpret_cast<const uint4 *>(
+        X + min((int64_t)wave * SHORT_STEP + blk * 16, (int64_t)K - 16));
+    const uint4 xlo = xs[0];
+    const uint4 xhi = xs[1];
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = min(wave * 16 + kk, nchunks - 1);
+    uint2 code[JR];
+    uint32_t sbits[JR];
+#pragma unroll
+    for (int j = 0; j < JR; ++j) {
+        const int64_t n = min(n0 + 4 * j + r, N - 1);
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(P + n * row_bytes + (int64_t)c * 8));
+        code[j] = make_uint2(v[0], v[1]);
+        sbits[j] = S[n * groups + (c >> 2)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. stage the step's activations, pair-interleaved ----
+    {
+        uint32_t pr[8];
+        interleave16(xlo, xhi, pr);
+        xw[(2 * (r & 1)) * 16 + kk] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        xw[(2 * (r & 1) + 1) * 16 + kk] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 3. decode + sign-select accumulate; the chunk lies inside one
+    //         128-weight block, whose scale (halved: the operands are +-2)
+    //         multiplies the chunk's sum ----
+    const uint32_t kact = opaque_mask(wave * 16 + kk < nchunks);
+    uint4 xq[4];   // blocks 2 kk (pieces 0, 1) and 2 kk + 1 (pieces 2, 3)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xq[q] = xw[q * 16 + kk];
+    float acc[JR];
+#pragma unroll
+    for (int j = 0; j < JR; ++j) {
+        const uint64_t v = sign_nz_fields64((uint64_t)code[j].x | ((uint64_t)code[j].y << 32));
+        float part = 0.f;
+        auto pair = [&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            uint32_t lo, hi;
+            weight_pairs2<I>(v, lo, hi);   // code word 0 -> block 2 kk, word 1 -> block 2 kk + 1
+            part = dot2<XBF16>(lo, (&xq[I >> 2].x)[I & 3], part);
+            part = dot2<XBF16>(hi, (&xq[2 + (I >> 2)].x)[I & 3], part);
+        };
+        pair(std::integral_constant<int, 0>{});
+        pair(std::integral_constant<int, 1>{});
+        pair(std::integral_constant<int, 2>{});
+        pair(std::integral_constant<int, 3>{});
+        pair(std::integral_constant<int, 4>{});
+        pair(std::integral_constant<int, 5>{});
+        pair(std::integral_constant<int, 6>{});
+        pair(std::integral_constant<int, 7>{});
+        const float s = f16_bits_to_float((uint16_t)sbits[j]) * 0.5f;
+        acc[j] = masked_fma(kact, s, part, 0.f);
+    }
+
+    // ---- 4. reduce over the 16 lanes of each DPP row, then across waves ----
+#pragma unroll
+    for (int j = 0; j < JR; ++j) acc[j] = row16_sum(acc[j]);
+    if (kk == 0) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j) red[wave * ROWS + 4 * j + r] = acc[j];
+    }
+    __syncthreads();
+    if (tid < ROWS) {
+        float y = 0.f;
+        for (int w = 0; w < nwaves; ++w) y += red[w * ROWS + tid];
+        const int n = n0 + tid;
+        if (n < N) store_out<YT>(Y, n, y);
+    }
+}
+
+template <bool XBF16, int YT, int JR>
+hipError_t launch_short_t(const GemmArgs &a) {
+    constexpr int ROWS = 4 * JR;
+    const int nwaves = (int)((a.K + SHORT_STEP - 1) / SHORT_STEP);
+    const size_t lds = (size_t)nwaves * SHORT_PIECES * 16 + (size_t)nwaves * ROWS * sizeof(float);
+    hipLaunchKernelGGL((gemv_short_kernel<XBF16, YT, JR>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
+                       dim3((unsigned)(64 * nwaves)), lds, a.stream, static_cast<const uint16_t *>(a.X), a.W,
+                       a.S, a.Y, (int)a.N, (int)a.K);
+    return hipGetLastError();
+}
+
+template <bool XBF16, int YT>
+hipError_t launch_short_j(const GemmArgs &a) {
+    switch ((a.N + 1023) / 1024) {
+    case 1: return launch_short_t<XBF16, YT, 1>(a);
+    case 2: return launch_short_t<XBF16, YT, 2>(a);
+    case 3: return launch_short_t<XBF16, YT, 3>(a);
+    case 4: return launch_short_t<XBF16, YT, 4>(a);
+    default: return launch_short_t<XBF16, YT, 5>(a);
+    }
+}
+
+hipError_t launch_short(const GemmArgs &a) {
+    const bool bf = a.x_dtype == 1;
+    switch (a.y_dtype) {
+    case 0: return bf ? launch_short_j<true, 0>(a) : launch_short_j<false, 0>(a);
+    case 1: return bf ? launch_short_j<true, 1>(a) : launch_short_j<false, 1>(a);
+    default: return bf ? launch_short_j<true, 2>(a) : launch_short_j<false, 2>(a);
+    }
+}
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) {
@@ -256,6 +409,7 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
 }
 
 hipError_t launch_gemv(const GemmArgs &a) {
+    if (a.M == 1 && a.Q == nullptr && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
     switch (a.M) {
     case 1: return launch_gemv_m<1>(a);
     case 2: return launch_gemv_m<2>(a);
