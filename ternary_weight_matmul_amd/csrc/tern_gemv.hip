@@ -24,9 +24,9 @@
 //     order (deterministic; no atomics, no workspace).
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
-// A short-step variant (gemv_short_kernel, below) serves M = 1 with fp16
-// scales when K and N are at most 5120: one workgroup per CU at most,
-// 512-weight steps and 8 code bytes per lane and row.
+// A short-step variant (gemv_short_kernel, below) serves M = 1 when K and N
+// are at most 5120: one workgroup per CU at most, 512-weight steps and 8
+// code bytes per lane and row.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -249,7 +249,7 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }
 
 
-// ---- short-step variant: M = 1, fp16 scales, K <= 5120, N <= 5120 ----
+// ---- short-step variant: M = 1, K <= 5120, N <= 5120 ----
 // The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
 // with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
 // CU gets the same share (8-row workgroups would leave half of the CUs with
@@ -268,10 +268,10 @@ constexpr int SHORT_PIECES = 64;  // 16-byte activation pieces per step
 constexpr int64_t kShortMaxK = 5120;
 constexpr int64_t kShortMaxN = 5120;
 
-template <bool XBF16, int YT, int JR>
+template <bool XBF16, int YT, int JR, bool S8>
 __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ P, const uint16_t *__restrict__ S,
-    void *__restrict__ Y, int N, int K) {
+    const int8_t *__restrict__ Q, const float *__restrict__ R, void *__restrict__ Y, int N, int K) {
     constexpr int ROWS = 4 * JR;
     extern __shared__ uint4 lds[];
     const int tid = threadIdx.x;
@@ -306,9 +306,16 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(P + n * row_bytes + (int64_t)c * 8));
         code[j] = make_uint2(v[0], v[1]);
-        sbits[j] = S[n * groups + (c >> 2)];
+        if constexpr (S8) sbits[j] = (uint32_t)(int32_t)Q[n * groups + (c >> 2)];
+        else sbits[j] = S[n * groups + (c >> 2)];
     }
     __builtin_amdgcn_sched_barrier(0);
+    // S8: the row factor multiplies the finished row sum; the threads that
+    // store rows fetch it now, off the critical path
+    float rowf = 1.f;
+    if constexpr (S8) {
+        if (tid < ROWS) rowf = R[min(n0 + tid, N - 1)];
+    }
 
     // ---- 2. stage the step's activations, pair-interleaved ----
     {
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
         pair(std::integral_constant<int, 5>{});
         pair(std::integral_constant<int, 6>{});
         pair(std::integral_constant<int, 7>{});
-        const float s = f16_bits_to_float((uint16_t)sbits[j]) * 0.5f;
+        const float s = (S8 ? (float)(int32_t)sbits[j] : f16_bits_to_float((uint16_t)sbits[j])) * 0.5f;
         acc[j] = masked_fma(kact, s, part, 0.f);
     }
 
@@ -363,40 +370,46 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
     if (tid < ROWS) {
         float y = 0.f;
         for (int w = 0; w < nwaves; ++w) y += red[w * ROWS + tid];
+        if constexpr (S8) y *= rowf;
         const int n = n0 + tid;
         if (n < N) store_out<YT>(Y, n, y);
     }
 }
 
-template <bool XBF16, int YT, int JR>
+template <bool XBF16, int YT, int JR, bool S8>
 hipError_t launch_short_t(const GemmArgs &a) {
     constexpr int ROWS = 4 * JR;
     const int nwaves = (int)((a.K + SHORT_STEP - 1) / SHORT_STEP);
     const size_t lds = (size_t)nwaves * SHORT_PIECES * 16 + (size_t)nwaves * ROWS * sizeof(float);
-    hipLaunchKernelGGL((gemv_short_kernel<XBF16, YT, JR>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
+    hipLaunchKernelGGL((gemv_short_kernel<XBF16, YT, JR, S8>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
                        dim3((unsigned)(64 * nwaves)), lds, a.stream, static_cast<const uint16_t *>(a.X), a.W,
-                       a.S, a.Y, (int)a.N, (int)a.K);
+                       a.S, a.Q, a.R, a.Y, (int)a.N, (int)a.K);
     return hipGetLastError();
 }
 
-template <bool XBF16, int YT>
+template <bool XBF16, int YT, bool S8>
 hipError_t launch_short_j(const GemmArgs &a) {
     switch ((a.N + 1023) / 1024) {
-    case 1: return launch_short_t<XBF16, YT, 1>(a);
-    case 2: return launch_short_t<XBF16, YT, 2>(a);
-    case 3: return launch_short_t<XBF16, YT, 3>(a);
-    case 4: return launch_short_t<XBF16, YT, 4>(a);
-    default: return launch_short_t<XBF16, YT, 5>(a);
+    case 1: return launch_short_t<XBF16, YT, 1, S8>(a);
+    case 2: return launch_short_t<XBF16, YT, 2, S8>(a);
+    case 3: return launch_short_t<XBF16, YT, 3, S8>(a);
+    case 4: return launch_short_t<XBF16, YT, 4, S8>(a);
+    default: return launch_short_t<XBF16, YT, 5, S8>(a);
+    }
+}
+
+template <bool S8>
+hipError_t launch_short_s(const GemmArgs &a) {
+    const bool bf = a.x_dtype == 1;
+    switch (a.y_dtype) {
+    case 0: return bf ? launch_short_j<true, 0, S8>(a) : launch_short_j<false, 0, S8>(a);
+    case 1: return bf ? launch_short_j<true, 1, S8>(a) : launch_short_j<false, 1, S8>(a);
+    default: return bf ? launch_short_j<true, 2, S8>(a) : launch_short_j<false, 2, S8>(a);
     }
 }
 
 hipError_t launch_short(const GemmArgs &a) {
-    const bool bf = a.x_dtype == 1;
-    switch (a.y_dtype) {
-    case 0: return bf ? launch_short_j<true, 0>(a) : launch_short_j<false, 0>(a);
-    case 1: return bf ? launch_short_j<true, 1>(a) : launch_short_j<false, 1>(a);
-    default: return bf ? launch_short_j<true, 2>(a) : launch_short_j<false, 2>(a);
-    }
+    return a.Q != nullptr ? launch_short_s<true>(a) : launch_short_s<false>(a);
 }
 }  // namespace
 
@@ -409,7 +422,7 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
 }
 
 hipError_t launch_gemv(const GemmArgs &a) {
-    if (a.M == 1 && a.Q == nullptr && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
+    if (a.M == 1 && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
     switch (a.M) {
     case 1: return launch_gemv_m<1>(a);
     case 2: return launch_gemv_m<2>(a);
