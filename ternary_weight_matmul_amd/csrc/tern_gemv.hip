@@ -267,8 +267,9 @@ constexpr int SHORT_CHUNK = 32;   // weights per lane per row (8 bytes)
 constexpr int SHORT_PIECES = 64;  // 16-byte activation pieces per step
 constexpr int64_t kShortMaxK = 5120;
 constexpr int64_t kShortMaxN = 5120;
+constexpr int64_t kShortMaxM = 2;
 
-template <bool XBF16, int YT, int JR, bool S8>
+template <int M, bool XBF16, int YT, int JR, bool S8>
 __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ P, const uint16_t *__restrict__ S,
     const int8_t *__restrict__ Q, const float *__restrict__ R, void *__restrict__ Y, int N, int K) {
@@ -284,18 +285,22 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
     const int64_t row_bytes = K >> 2;
     const int groups = K >> 7;
     const int nchunks = K / SHORT_CHUNK;
-    uint4 *xw = lds + wave * SHORT_PIECES;
-    float *red = reinterpret_cast<float *>(lds + nwaves * SHORT_PIECES);
+    uint4 *xw = lds + wave * (M * SHORT_PIECES);
+    float *red = reinterpret_cast<float *>(lds + nwaves * (M * SHORT_PIECES));
 
     // ---- 1. loads, all unconditional at clamped in-bounds addresses: the
     //         activation block this lane stages first, then codes and scales
     //         (the scheduling barriers keep that order, so the staging waits
     //         for the activations alone) ----
     const int blk = 2 * kk + (r & 1);   // 16-element block of this step
-    const uint4 *xs = reinterpret_cast<const uint4 *>(
-        X + min((int64_t)wave * SHORT_STEP + blk * 16, (int64_t)K - 16));
-    const uint4 xlo = xs[0];
-    const uint4 xhi = xs[1];
+    const int64_t xoff = min((int64_t)wave * SHORT_STEP + blk * 16, (int64_t)K - 16);
+    uint4 xraw[M][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint4 *xs = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + xoff);
+        xraw[m][0] = xs[0];
+        xraw[m][1] = xs[1];
+    }
     __builtin_amdgcn_sched_barrier(0);
     const int c = min(wave * 16 + kk, nchunks - 1);
     uint2 code[JR];
@@ -314,15 +319,17 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
     // store rows fetch it now, off the critical path
     float rowf = 1.f;
     if constexpr (S8) {
-        if (tid < ROWS) rowf = R[min(n0 + tid, N - 1)];
+        if (tid < ROWS * M) rowf = R[min(n0 + tid % ROWS, N - 1)];
     }
 
     // ---- 2. stage the step's activations, pair-interleaved ----
-    {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
         uint32_t pr[8];
-        interleave16(xlo, xhi, pr);
-        xw[(2 * (r & 1)) * 16 + kk] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-        xw[(2 * (r & 1) + 1) * 16 + kk] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+        interleave16(xraw[m][0], xraw[m][1], pr);
+        uint4 *dst = xw + m * SHORT_PIECES;
+        dst[(2 * (r & 1)) * 16 + kk] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        dst[(2 * (r & 1) + 1) * 16 + kk] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -332,20 +339,27 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
     //         128-weight block, whose scale (halved: the operands are +-2)
     //         multiplies the chunk's sum ----
     const uint32_t kact = opaque_mask(wave * 16 + kk < nchunks);
-    uint4 xq[4];   // blocks 2 kk (pieces 0, 1) and 2 kk + 1 (pieces 2, 3)
+    uint4 xq[M][4];   // per row m: blocks 2 kk (pieces 0, 1) and 2 kk + 1 (pieces 2, 3)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xq[q] = xw[q * 16 + kk];
-    float acc[JR];
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xq[m][q] = xw[m * SHORT_PIECES + q * 16 + kk];
+    float acc[JR][M];
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
         const uint64_t v = sign_nz_fields64((uint64_t)code[j].x | ((uint64_t)code[j].y << 32));
-        float part = 0.f;
+        float part[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[m] = 0.f;
         auto pair = [&](auto ic) {
             constexpr int I = decltype(ic)::value;
             uint32_t lo, hi;
             weight_pairs2<I>(v, lo, hi);   // code word 0 -> block 2 kk, word 1 -> block 2 kk + 1
-            part = dot2<XBF16>(lo, (&xq[I >> 2].x)[I & 3], part);
-            part = dot2<XBF16>(hi, (&xq[2 + (I >> 2)].x)[I & 3], part);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {   // each decoded pair feeds every activation row
+                part[m] = dot2<XBF16>(lo, (&xq[m][I >> 2].x)[I & 3], part[m]);
+                part[m] = dot2<XBF16>(hi, (&xq[m][2 + (I >> 2)].x)[I & 3], part[m]);
+            }
         };
         pair(std::integral_constant<int, 0>{});
         pair(std::integral_constant<int, 1>{});
@@ -356,60 +370,72 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
         pair(std::integral_constant<int, 6>{});
         pair(std::integral_constant<int, 7>{});
         const float s = (S8 ? (float)(int32_t)sbits[j] : f16_bits_to_float((uint16_t)sbits[j])) * 0.5f;
-        acc[j] = masked_fma(kact, s, part, 0.f);
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[j][m] = masked_fma(kact, s, part[m], 0.f);
     }
 
     // ---- 4. reduce over the 16 lanes of each DPP row, then across waves ----
 #pragma unroll
-    for (int j = 0; j < JR; ++j) acc[j] = row16_sum(acc[j]);
+    for (int j = 0; j < JR; ++j)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[j][m] = row16_sum(acc[j][m]);
     if (kk == 0) {
 #pragma unroll
-        for (int j = 0; j < JR; ++j) red[wave * ROWS + 4 * j + r] = acc[j];
+        for (int j = 0; j < JR; ++j)
+#pragma unroll
+            for (int m = 0; m < M; ++m) red[(wave * ROWS + 4 * j + r) * M + m] = acc[j][m];
     }
     __syncthreads();
-    if (tid < ROWS) {
+    if (tid < ROWS * M) {
+        const int row = tid % ROWS;
+        const int m = tid / ROWS;
         float y = 0.f;
-        for (int w = 0; w < nwaves; ++w) y += red[w * ROWS + tid];
+        for (int w = 0; w < nwaves; ++w) y += red[(w * ROWS + row) * M + m];
         if constexpr (S8) y *= rowf;
-        const int n = n0 + tid;
-        if (n < N) store_out<YT>(Y, n, y);
+        const int n = n0 + row;
+        if (n < N) store_out<YT>(Y, (int64_t)m * N + n, y);
     }
 }
 
-template <bool XBF16, int YT, int JR, bool S8>
+template <int M, bool XBF16, int YT, int JR, bool S8>
 hipError_t launch_short_t(const GemmArgs &a) {
     constexpr int ROWS = 4 * JR;
     const int nwaves = (int)((a.K + SHORT_STEP - 1) / SHORT_STEP);
-    const size_t lds = (size_t)nwaves * SHORT_PIECES * 16 + (size_t)nwaves * ROWS * sizeof(float);
-    hipLaunchKernelGGL((gemv_short_kernel<XBF16, YT, JR, S8>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
+    const size_t lds = (size_t)nwaves * M * SHORT_PIECES * 16 + (size_t)nwaves * ROWS * M * sizeof(float);
+    hipLaunchKernelGGL((gemv_short_kernel<M, XBF16, YT, JR, S8>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
                        dim3((unsigned)(64 * nwaves)), lds, a.stream, static_cast<const uint16_t *>(a.X), a.W,
                        a.S, a.Q, a.R, a.Y, (int)a.N, (int)a.K);
     return hipGetLastError();
 }
 
-template <bool XBF16, int YT, bool S8>
+template <int M, bool XBF16, int YT, bool S8>
 hipError_t launch_short_j(const GemmArgs &a) {
     switch ((a.N + 1023) / 1024) {
-    case 1: return launch_short_t<XBF16, YT, 1, S8>(a);
-    case 2: return launch_short_t<XBF16, YT, 2, S8>(a);
-    case 3: return launch_short_t<XBF16, YT, 3, S8>(a);
-    case 4: return launch_short_t<XBF16, YT, 4, S8>(a);
-    default: return launch_short_t<XBF16, YT, 5, S8>(a);
+    case 1: return launch_short_t<M, XBF16, YT, 1, S8>(a);
+    case 2: return launch_short_t<M, XBF16, YT, 2, S8>(a);
+    case 3: return launch_short_t<M, XBF16, YT, 3, S8>(a);
+    case 4: return launch_short_t<M, XBF16, YT, 4, S8>(a);
+    default: return launch_short_t<M, XBF16, YT, 5, S8>(a);
     }
 }
 
-template <bool S8>
+template <int M, bool S8>
 hipError_t launch_short_s(const GemmArgs &a) {
     const bool bf = a.x_dtype == 1;
     switch (a.y_dtype) {
-    case 0: return bf ? launch_short_j<true, 0, S8>(a) : launch_short_j<false, 0, S8>(a);
-    case 1: return bf ? launch_short_j<true, 1, S8>(a) : launch_short_j<false, 1, S8>(a);
-    default: return bf ? launch_short_j<true, 2, S8>(a) : launch_short_j<false, 2, S8>(a);
+    case 0: return bf ? launch_short_j<M, true, 0, S8>(a) : launch_short_j<M, false, 0, S8>(a);
+    case 1: return bf ? launch_short_j<M, true, 1, S8>(a) : launch_short_j<M, false, 1, S8>(a);
+    default: return bf ? launch_short_j<M, true, 2, S8>(a) : launch_short_j<M, false, 2, S8>(a);
     }
 }
 
+template <int M>
+hipError_t launch_short_m(const GemmArgs &a) {
+    return a.Q != nullptr ? launch_short_s<M, true>(a) : launch_short_s<M, false>(a);
+}
+
 hipError_t launch_short(const GemmArgs &a) {
-    return a.Q != nullptr ? launch_short_s<true>(a) : launch_short_s<false>(a);
+    return a.M == 1 ? launch_short_m<1>(a) : launch_short_m<2>(a);
 }
 }  // namespace
 
@@ -422,7 +448,7 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
 }
 
 hipError_t launch_gemv(const GemmArgs &a) {
-    if (a.M == 1 && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
+    if (a.M <= kShortMaxM && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
     switch (a.M) {
     case 1: return launch_gemv_m<1>(a);
     case 2: return launch_gemv_m<2>(a);

@@ -60,8 +60,8 @@ RAGGED = [(1, 128, 1), (1, 640, 33), (3, 1152, 50), (4, 3200, 29), (1, 17408, 5)
           (17, 640, 100), (130, 384, 257), (64, 128, 512), (257, 640, 300), (1000, 256, 70),
           # small-M MFMA with 8 and 16 staged rows; with fp16 X, 128 x 128 tiles of two K groups
           (8, 4096, 200), (16, 2048, 300), (3000, 384, 1100),
-          # M = 1, K and N <= 5120: the short-step decode kernel at each row count
-          (1, 4992, 1025), (1, 2048, 2100), (1, 5120, 3071), (1, 1152, 5120)]
+          # M <= 2, K and N <= 5120: the short-step decode kernel at each row count
+          (1, 4992, 1025), (1, 2048, 2100), (1, 5120, 3071), (1, 1152, 5120), (2, 5120, 4097), (2, 640, 33)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
@@ -93,7 +93,7 @@ def test_matmul_s8_workloads(cfg, shape_id):
 
 
 @pytest.mark.parametrize("M,K,N,xd", [(3, 2048, 72, "bf16"), (200, 1024, 80, "f16"), (3, 2048, 72, "f16"),
-                                      (1, 5120, 4500, "bf16"), (1, 640, 33, "f16")])
+                                      (1, 5120, 4500, "bf16"), (1, 640, 33, "f16"), (2, 3072, 1500, "bf16")])
 def test_matmul_s8_exact_bit_exact(M, K, N, xd):
     """Integer activations, power-of-two row factors: every product and sum is
     exact in fp32, so the output equals the oracle rounded, bit for bit.

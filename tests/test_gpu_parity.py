@@ -147,18 +147,19 @@ def test_ragged_shapes(M, K, N, xd, yd):
         _full(p, path)
 
 
-# M = 1 with fp16 scales, K <= 5120 and N <= 5120: the short-step decode
-# kernel (4 JR rows per workgroup, JR = ceil(N / 1024), 512-weight steps);
-# each JR, K off the 512 grid, ragged last workgroups, both size limits and
-# the shapes just past them (the 8-row kernel)
+# M <= 2, K <= 5120 and N <= 5120: the short-step decode kernel (4 JR rows
+# per workgroup, JR = ceil(N / 1024), 512-weight steps); each JR, K off the
+# 512 grid, ragged last workgroups, both size limits and the shapes just
+# past them (the 8-row kernel)
 SHORT = [(128, 1), (640, 33), (1152, 1023), (4992, 1025), (2048, 2100), (3968, 3071), (5120, 4097),
          (5120, 5120), (384, 5119), (5248, 700), (5120, 5121)]
 
 
 @pytest.mark.parametrize("K,N", SHORT)
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("xd,yd", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f16")])
-def test_short_step_decode(K, N, xd, yd):
-    p = workloads.make_custom(K * 3 + N, 1, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.02)
+def test_short_step_decode(M, K, N, xd, yd):
+    p = workloads.make_custom(K * 3 + N + M, M, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.02)
     for path in ("auto", "gemv"):
         _full(p, path)
 
@@ -221,7 +222,7 @@ def test_scales_near_fp16_max_and_negative(M, path, xd):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (3, 2048, 40), (40, 1024, 80), (1, 4096, 16), (200, 1024, 80),
-                                   (1, 5120, 1100), (1, 640, 4500),
+                                   (1, 5120, 1100), (1, 640, 4500), (2, 5120, 2100),
                                    (2, 2048, 24), (2, 9216, 24), (4, 10240, 16), (1, 17408, 12), (8, 3072, 48),
                                    (16, 2048, 40)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
