@@ -24,8 +24,8 @@
 //     order (deterministic; no atomics, no workspace).
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
-// A short-step variant (gemv_short_kernel, below) serves M = 1 when K and N
-// are at most 5120: one workgroup per CU at most, 512-weight steps and 8
+// A short-step variant (gemv_short_kernel, below) serves M <= 2 when K and
+// N are at most 5120: one workgroup per CU at most, 512-weight steps and 8
 // code bytes per lane and row.
 #include <hip/hip_runtime.h>
 
@@ -249,7 +249,7 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }
 
 
-// ---- short-step variant: M = 1, K <= 5120, N <= 5120 ----
+// ---- short-step variant: M <= 2, K <= 5120, N <= 5120 ----
 // The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
 // with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
 // CU gets the same share (8-row workgroups would leave half of the CUs with
