@@ -78,7 +78,7 @@ bool gemv_fits(int64_t M, int64_t K) {
 // The automatic choice: the VALU decode kernel for one or two activation
 // rows; from three rows on, the MFMA kernel (16-row tiles: its time hardly
 // changes up to M = 16) is faster.  Measured on the 5120 / 17408 decode
-// shapes: M = 2 GEMV 5.3 / 12.5 / 13.6 us against MFMA 7.4 / 15.8 / 16.4;
+// shapes: M = 2 GEMV 4.6 / 12.5 / 13.6 us against MFMA 7.4 / 15.8 / 16.4;
 // M = 3 GEMV 7.6 / 18.8 / 19.9 against MFMA 7.5 / 15.9 / 16.6.
 constexpr int64_t kAutoGemvMaxM = 2;
 
