@@ -82,7 +82,13 @@ bool gemv_fits(int64_t M, int64_t K) {
 // M = 3 GEMV 7.6 / 18.8 / 19.9 against MFMA 7.5 / 15.9 / 16.6.
 constexpr int64_t kAutoGemvMaxM = 2;
 
-bool auto_gemv(int64_t M, int64_t K) { return M <= kAutoGemvMaxM && gemv_fits(M, K); }
+// Up to M = 4 the decode kernel also wins where it takes its short-step form
+// (K, N <= 5120; bf16, graph-timed): 5120 -> 5120 at M = 3 / 4 5.3 / 6.1 us
+// against MFMA 6.9 / 7.0, 5120 -> 1024 at M = 4 3.8 against 5.7, 4096 ->
+// 4096 4.4 against 5.6.
+bool auto_gemv(int64_t M, int64_t N, int64_t K) {
+    return (M <= kAutoGemvMaxM && gemv_fits(M, K)) || tern::gemv_short(M, N, K);
+}
 
 }  // namespace
 
@@ -129,7 +135,7 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
     if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
 
     const tern::GemmArgs a = make_args(X, x_dtype, packed_W, scales, nullptr, nullptr, Y, y_dtype, M, N, K, stream);
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, N, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 
@@ -167,7 +173,7 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
 
     const tern::GemmArgs a =
         make_args(X, x_dtype, packed_W, nullptr, scales_q, row_factor, Y, y_dtype, M, N, K, stream);
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, K));
+    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, N, K));
     return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
 }
 

@@ -24,9 +24,9 @@
 //     order (deterministic; no atomics, no workspace).
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
-// A short-step variant (gemv_short_kernel, below) serves M <= 2 when K and
+// A short-step variant (gemv_short_kernel, below) serves M <= 4 when K and
 // N are at most 5120: one workgroup per CU at most, 512-weight steps and 8
-// code bytes per lane and row.
+// code bytes per lane and row; each decoded pair feeds every activation row.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -249,7 +249,7 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }
 
 
-// ---- short-step variant: M <= 2, K <= 5120, N <= 5120 ----
+// ---- short-step variant: M <= 4, K <= 5120, N <= 5120 ----
 // The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
 // with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
 // CU gets the same share (8-row workgroups would leave half of the CUs with
@@ -267,7 +267,7 @@ constexpr int SHORT_CHUNK = 32;   // weights per lane per row (8 bytes)
 constexpr int SHORT_PIECES = 64;  // 16-byte activation pieces per step
 constexpr int64_t kShortMaxK = 5120;
 constexpr int64_t kShortMaxN = 5120;
-constexpr int64_t kShortMaxM = 2;
+constexpr int64_t kShortMaxM = 4;
 
 template <int M, bool XBF16, int YT, int JR, bool S8>
 __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_kernel(
@@ -386,14 +386,21 @@ __global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_ker
             for (int m = 0; m < M; ++m) red[(wave * ROWS + 4 * j + r) * M + m] = acc[j][m];
     }
     __syncthreads();
-    if (tid < ROWS * M) {
-        const int row = tid % ROWS;
-        const int m = tid / ROWS;
+    auto finish = [&](int o, float f) {   // output o = m * ROWS + row, row factor f
+        const int row = o % ROWS;
+        const int m = o / ROWS;
         float y = 0.f;
         for (int w = 0; w < nwaves; ++w) y += red[(w * ROWS + row) * M + m];
-        if constexpr (S8) y *= rowf;
+        if constexpr (S8) y *= f;
         const int n = n0 + row;
         if (n < N) store_out<YT>(Y, (int64_t)m * N + n, y);
+    };
+    if constexpr (ROWS * M <= 64) {
+        if (tid < ROWS * M) finish(tid, rowf);
+    } else {
+        // more outputs than one wave has threads (M = 4, 20 rows, K <= 512)
+        for (int o = tid; o < ROWS * M; o += blockDim.x)
+            finish(o, o == tid ? rowf : (S8 ? R[min(n0 + o % ROWS, N - 1)] : 1.f));
     }
 }
 
@@ -435,7 +442,12 @@ hipError_t launch_short_m(const GemmArgs &a) {
 }
 
 hipError_t launch_short(const GemmArgs &a) {
-    return a.M == 1 ? launch_short_m<1>(a) : launch_short_m<2>(a);
+    switch (a.M) {
+    case 1: return launch_short_m<1>(a);
+    case 2: return launch_short_m<2>(a);
+    case 3: return launch_short_m<3>(a);
+    default: return launch_short_m<4>(a);
+    }
 }
 }  // namespace
 
@@ -447,8 +459,12 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
     return g.lds;
 }
 
+bool gemv_short(int64_t M, int64_t N, int64_t K) {
+    return M >= 1 && M <= kShortMaxM && K <= kShortMaxK && N <= kShortMaxN;
+}
+
 hipError_t launch_gemv(const GemmArgs &a) {
-    if (a.M <= kShortMaxM && a.K <= kShortMaxK && a.N <= kShortMaxN) return launch_short(a);
+    if (gemv_short(a.M, a.N, a.K)) return launch_short(a);
     switch (a.M) {
     case 1: return launch_gemv_m<1>(a);
     case 2: return launch_gemv_m<2>(a);

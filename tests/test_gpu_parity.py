@@ -156,7 +156,7 @@ SHORT = [(128, 1), (640, 33), (1152, 1023), (4992, 1025), (2048, 2100), (3968, 3
 
 
 @pytest.mark.parametrize("K,N", SHORT)
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("xd,yd", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f16")])
 def test_short_step_decode(M, K, N, xd, yd):
     p = workloads.make_custom(K * 3 + N + M, M, K, N, x_dtype=xd, y_dtype=yd, reserved_rate=0.02)
