@@ -57,7 +57,7 @@ typedef enum { TERN_F16 = 0, TERN_BF16 = 1, TERN_F32 = 2 } tern_dtype;
 /* Which kernel family computes tern_matmul_path's result. */
 typedef enum {
     TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): GEMV for M <= 2, and for
-                           M <= 4 with K, N <= 5120; else MFMA */
+                           M <= 4 with N <= 5120 and K <= 8192; else MFMA */
     TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
     TERN_PATH_MFMA = 2  /* LDS-staged activations + in-register weight decode + MFMA; any M */
 } tern_path;

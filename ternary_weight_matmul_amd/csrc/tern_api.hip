@@ -83,9 +83,9 @@ bool gemv_fits(int64_t M, int64_t K) {
 constexpr int64_t kAutoGemvMaxM = 2;
 
 // Up to M = 4 the decode kernel also wins where it takes its short-step form
-// (K, N <= 5120; bf16, graph-timed): 5120 -> 5120 at M = 3 / 4 5.3 / 6.1 us
-// against MFMA 6.9 / 7.0, 5120 -> 1024 at M = 4 3.8 against 5.7, 4096 ->
-// 4096 4.4 against 5.6.
+// (N <= 5120, K <= 8192; bf16, graph-timed): 5120 -> 5120 at M = 3 / 4
+// 5.3 / 6.1 us against MFMA 6.9 / 7.0, 5120 -> 1024 at M = 4 3.8 against
+// 5.7, 6144 -> 5120 at M = 3 / 4 5.5 / 6.3 against 8.8 / 8.8.
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
     return (M <= kAutoGemvMaxM && gemv_fits(M, K)) || tern::gemv_short(M, N, K);
 }

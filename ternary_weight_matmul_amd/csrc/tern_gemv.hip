@@ -24,9 +24,10 @@
 //     order (deterministic; no atomics, no workspace).
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
-// A short-step variant (gemv_short_kernel, below) serves M <= 4 when K and
-// N are at most 5120: one workgroup per CU at most, 512-weight steps and 8
-// code bytes per lane and row; each decoded pair feeds every activation row.
+// A short-step variant (gemv_short_kernel, below) serves M <= 4 when N is at
+// most 5120 and K at most 5120 (M = 1) or 8192: one workgroup per CU at
+// most, 512-weight steps and 8 code bytes per lane and row; each decoded
+// pair feeds every activation row.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -249,28 +250,31 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }
 
 
-// ---- short-step variant: M <= 4, K <= 5120, N <= 5120 ----
+// ---- short-step variant: M <= 4, N <= 5120, K <= 5120 (M = 1) or 8192 ----
 // The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
 // with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
 // CU gets the same share (8-row workgroups would leave half of the CUs with
 // one workgroup more than the others).  Each wave takes one 512-weight step,
-// so a workgroup has ceil(K / 512) <= 10 waves, and lane (r, kk) reads the
+// so a workgroup has ceil(K / 512) <= 16 waves, and lane (r, kk) reads the
 // 8 code bytes (32 weights) of chunk kk of rows n0 + 4j + r.  The step's
 // activations (32 blocks of 16) are staged pair-interleaved in the wave's
 // LDS slice by lanes r = 0, 1; lanes r = 2, 3 write the same words again.
 // Measured at M = 1, bf16 (graph-timed, weights rotated), against the kernel
 // above: 5120 -> 5120 3.98 -> 3.94 us (4.22 -> 4.07 with bench.py's 2 GB
 // of rotated weights), 5120 -> 3072 3.58 -> 3.32, 2048 -> 5120 3.01 -> 2.88;
-// at K = 8192 or N = 6144 it was no better or slower.
+// at K = 8192 or N = 6144 it was no better or slower.  From M = 2 it beat
+// the 8-row kernel and the MFMA kernel on every shape tried up to K = 8192
+// (e.g. M = 3, 6144 -> 5120: 8.77 -> 5.53 us), hence the longer K there.
 constexpr int SHORT_STEP = 512;   // weights of one row per wave
 constexpr int SHORT_CHUNK = 32;   // weights per lane per row (8 bytes)
 constexpr int SHORT_PIECES = 64;  // 16-byte activation pieces per step
-constexpr int64_t kShortMaxK = 5120;
+constexpr int64_t kShortMaxK = 5120;       // M = 1
+constexpr int64_t kShortMaxKWide = 8192;   // M = 2 .. 4
 constexpr int64_t kShortMaxN = 5120;
 constexpr int64_t kShortMaxM = 4;
 
 template <int M, bool XBF16, int YT, int JR, bool S8>
-__global__ __launch_bounds__(64 * (kShortMaxK / SHORT_STEP)) void gemv_short_kernel(
+__global__ __launch_bounds__(64 * ((M == 1 ? kShortMaxK : kShortMaxKWide) / SHORT_STEP)) void gemv_short_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ P, const uint16_t *__restrict__ S,
     const int8_t *__restrict__ Q, const float *__restrict__ R, void *__restrict__ Y, int N, int K) {
     constexpr int ROWS = 4 * JR;
@@ -409,6 +413,19 @@ hipError_t launch_short_t(const GemmArgs &a) {
     constexpr int ROWS = 4 * JR;
     const int nwaves = (int)((a.K + SHORT_STEP - 1) / SHORT_STEP);
     const size_t lds = (size_t)nwaves * M * SHORT_PIECES * 16 + (size_t)nwaves * ROWS * M * sizeof(float);
+    if (lds > 64 * 1024) {   // M = 4 with K > 7168: raise the dynamic-LDS limit once per device
+        static std::atomic<uint64_t> done_mask{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = 1ull << (dev & 63);
+        if (!(done_mask.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_short_kernel<M, XBF16, YT, JR, S8>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            done_mask.fetch_or(bit, std::memory_order_acq_rel);
+        }
+    }
     hipLaunchKernelGGL((gemv_short_kernel<M, XBF16, YT, JR, S8>), dim3((unsigned)((a.N + ROWS - 1) / ROWS)),
                        dim3((unsigned)(64 * nwaves)), lds, a.stream, static_cast<const uint16_t *>(a.X), a.W,
                        a.S, a.Q, a.R, a.Y, (int)a.N, (int)a.K);
@@ -460,7 +477,7 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
 }
 
 bool gemv_short(int64_t M, int64_t N, int64_t K) {
-    return M >= 1 && M <= kShortMaxM && K <= kShortMaxK && N <= kShortMaxN;
+    return M >= 1 && M <= kShortMaxM && K <= (M == 1 ? kShortMaxK : kShortMaxKWide) && N <= kShortMaxN;
 }
 
 hipError_t launch_gemv(const GemmArgs &a) {

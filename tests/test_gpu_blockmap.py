@@ -73,12 +73,12 @@ def test_skip_matches_oracle(M, K, N, rate):
 
 # K a multiple of 1024 (whole wave steps): with a partial last step the list
 # hands its chunks to other lanes, and the 16-lane sum associates differently.
-# K > 5120, so the dense call takes the decode kernel whose layout the
-# skipping kernel follows (at K, N <= 5120 the short-step kernel, which sums
-# in another order, serves M <= 2).  The skipping kernel serves M <= 2; from
-# M = 3 on the call is tern_matmul.
-@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 6144, 512, "bf16", "bf16"), (2, 6144, 77, "f16", "f16"),
-                                         (1, 17408, 40, "bf16", "f32"), (2, 7168, 50, "f16", "f32")])
+# K past the short-step kernel's limit (5120 at M = 1, 8192 at M = 2), so the
+# dense call takes the decode kernel whose layout the skipping kernel
+# follows (the short-step kernel sums in another order).  The skipping
+# kernel serves M <= 2; from M = 3 on the call is tern_matmul.
+@pytest.mark.parametrize("M,K,N,xd,yd", [(1, 6144, 512, "bf16", "bf16"), (2, 9216, 77, "f16", "f16"),
+                                         (1, 17408, 40, "bf16", "f32"), (2, 10240, 50, "f16", "f32")])
 def test_all_marked_equals_dense_kernel_bit_for_bit(M, K, N, xd, yd):
     p = _sparse_problem(M + K + N, M, K, N, 0.5, xd=xd, yd=yd)
     x, w, s = _dev(p)

@@ -63,7 +63,7 @@ RAGGED = [(1, 128, 1), (1, 640, 33), (3, 1152, 50), (4, 3200, 29), (1, 17408, 5)
           # M <= 2, K and N <= 5120: the short-step decode kernel at each row count
           (1, 4992, 1025), (1, 2048, 2100), (1, 5120, 3071), (1, 1152, 5120), (2, 5120, 4097), (2, 640, 33),
           # M = 4 with one wave per workgroup: 80 outputs for 64 threads
-          (4, 384, 4500), (3, 5120, 2000)]
+          (4, 384, 4500), (3, 5120, 2000), (4, 8192, 1500), (2, 7296, 700)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)

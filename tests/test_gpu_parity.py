@@ -147,12 +147,14 @@ def test_ragged_shapes(M, K, N, xd, yd):
         _full(p, path)
 
 
-# M <= 2, K <= 5120 and N <= 5120: the short-step decode kernel (4 JR rows
-# per workgroup, JR = ceil(N / 1024), 512-weight steps); each JR, K off the
-# 512 grid, ragged last workgroups, both size limits and the shapes just
-# past them (the 8-row kernel)
+# M <= 4, N <= 5120, K <= 5120 (M = 1) or 8192: the short-step decode kernel
+# (4 JR rows per workgroup, JR = ceil(N / 1024), 512-weight steps); each JR,
+# K off the 512 grid, ragged last workgroups, the size limits and the
+# shapes just past them (the 8-row or the MFMA kernel)
 SHORT = [(128, 1), (640, 33), (1152, 1023), (4992, 1025), (2048, 2100), (3968, 3071), (5120, 4097),
-         (5120, 5120), (384, 5119), (5248, 700), (5120, 5121)]
+         (5120, 5120), (384, 5119), (5248, 700), (5120, 5121),
+         # from M = 2 up to K = 8192 (16 waves; M = 4 past K = 7168 needs more than 64 KB of LDS)
+         (6272, 3000), (8192, 5120), (7296, 129), (8320, 300)]
 
 
 @pytest.mark.parametrize("K,N", SHORT)
