@@ -272,6 +272,12 @@ constexpr int64_t kShortMaxK = 5120;       // M = 1
 constexpr int64_t kShortMaxKWide = 8192;   // M = 2 .. 4
 constexpr int64_t kShortMaxN = 5120;
 constexpr int64_t kShortMaxM = 4;
+// M = 2 also takes it on layers of at least 12288 rows (2.4 or more rounds of
+// 20-row workgroups over the CUs), against the 8-row kernel: 5120 -> 15360
+// 10.53 -> 8.9 us, 5120 -> 17408 11.78 -> 10.7 us; with 1.2 rounds
+// (5120 -> 6144) it was slower, 5.10 -> 6.45 us, and at M = 3, 4 it lost to
+// the MFMA kernel at every N past 5120 tried.
+constexpr int64_t kShortMinNRounds = 12288;
 
 template <int M, bool XBF16, int YT, int JR, bool S8>
 __global__ __launch_bounds__(64 * ((M == 1 ? kShortMaxK : kShortMaxKWide) / SHORT_STEP)) void gemv_short_kernel(
@@ -477,6 +483,7 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) {
 }
 
 bool gemv_short(int64_t M, int64_t N, int64_t K) {
+    if (M == 2 && K <= kShortMaxKWide && N >= kShortMinNRounds) return true;
     return M >= 1 && M <= kShortMaxM && K <= (M == 1 ? kShortMaxK : kShortMaxKWide) && N <= kShortMaxN;
 }
 

@@ -26,7 +26,8 @@ hipError_t launch_gemv(const GemmArgs &a);
 // LDS bytes the GEMV needs for this M, K (it stages X[M,K] on chip).
 size_t gemv_lds_bytes(int64_t M, int64_t K);
 // True when launch_gemv takes its short-step kernel (M <= 4, N <= 5120, and
-// K <= 5120 at M = 1 or K <= 8192 at M = 2 .. 4).
+// K <= 5120 at M = 1 or K <= 8192 at M = 2 .. 4; also M = 2, K <= 8192,
+// N >= 12288).
 bool gemv_short(int64_t M, int64_t N, int64_t K);
 
 // Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 2).

@@ -154,7 +154,9 @@ def test_ragged_shapes(M, K, N, xd, yd):
 SHORT = [(128, 1), (640, 33), (1152, 1023), (4992, 1025), (2048, 2100), (3968, 3071), (5120, 4097),
          (5120, 5120), (384, 5119), (5248, 700), (5120, 5121),
          # from M = 2 up to K = 8192 (16 waves; M = 4 past K = 7168 needs more than 64 KB of LDS)
-         (6272, 3000), (8192, 5120), (7296, 129), (8320, 300)]
+         (6272, 3000), (8192, 5120), (7296, 129), (8320, 300),
+         # M = 2 on layers of 12288 rows or more (several rounds of workgroups)
+         (5120, 12289), (2048, 20000), (8192, 12288)]
 
 
 @pytest.mark.parametrize("K,N", SHORT)
