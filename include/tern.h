@@ -59,7 +59,14 @@ typedef enum {
     TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): GEMV for M <= 2, and for
                            M <= 4 with N <= 5120 and K <= 8192; else MFMA */
     TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
-    TERN_PATH_MFMA = 2  /* LDS-staged activations + in-register weight decode + MFMA; any M */
+    TERN_PATH_MFMA = 2, /* LDS-staged activations + in-register weight decode + MFMA; any M */
+    TERN_PATH_GEMV_MFMA = 3, /* decode kernel whose sign-select sums run on the matrix cores
+                                (v_mfma_f32_4x4x4_16b on +-2 / 0 operands); M <= 4, with
+                                the activations X[M,K] staged whole in LDS */
+    TERN_PATH_GEMV_FP4 = 4  /* decode kernel with the weights as 4-bit (e2m1 +-2 / 0) matrix-core
+                               operands and each bf16 activation split exactly into two e4m3
+                               terms with a power-of-two scale per 32 (v_mfma_scale_f32_
+                               16x16x128_f8f6f4); bf16 X only, M <= 4, X staged whole in LDS */
 } tern_path;
 
 #define TERN_GROUP 128
@@ -112,8 +119,9 @@ tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed
  * tern_matmul_path -- tern_matmul with an explicit kernel choice.  Same
  * arguments, layouts and result contract as tern_matmul; `path` picks the
  * kernel family (for tests that compare the two, and for benchmarks).
- * TERN_PATH_GEMV with M > TERN_GEMV_MAX_M, or with an activation block too
- * large for on-chip staging, returns TERN_ERR_UNSUPPORTED.
+ * TERN_PATH_GEMV, TERN_PATH_GEMV_MFMA or TERN_PATH_GEMV_FP4 with M >
+ * TERN_GEMV_MAX_M, or with an activation block too large for on-chip staging,
+ * and TERN_PATH_GEMV_FP4 with fp16 activations, return TERN_ERR_UNSUPPORTED.
  */
 tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
                              const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M,

@@ -90,6 +90,30 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K) {
     return (M <= kAutoGemvMaxM && gemv_fits(M, K)) || tern::gemv_short(M, N, K);
 }
 
+// A forced path that cannot run this shape is TERN_ERR_UNSUPPORTED (checked
+// before anything is launched).
+tern_status check_path(tern_path path, tern_dtype x_dtype, int64_t M, int64_t N, int64_t K) {
+    if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA && path != TERN_PATH_GEMV_MFMA &&
+        path != TERN_PATH_GEMV_FP4)
+        return TERN_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0 || K == 0) return TERN_OK;
+    if (path == TERN_PATH_GEMV && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
+    if (path == TERN_PATH_GEMV_MFMA && !tern::gemv_mfma_fits(M, N, K)) return TERN_ERR_UNSUPPORTED;
+    if (path == TERN_PATH_GEMV_FP4 && !tern::gemv_fp4_fits(M, N, K, x_dtype == TERN_BF16 ? 1 : 0))
+        return TERN_ERR_UNSUPPORTED;
+    return TERN_OK;
+}
+
+hipError_t dispatch(const tern::GemmArgs &a, tern_path path) {
+    switch (path) {
+    case TERN_PATH_GEMV: return tern::launch_gemv(a);
+    case TERN_PATH_MFMA: return tern::launch_gemm(a);
+    case TERN_PATH_GEMV_MFMA: return tern::launch_gemv_mfma(a);
+    case TERN_PATH_GEMV_FP4: return tern::launch_gemv_fp4(a);
+    default: return auto_gemv(a.M, a.N, a.K) ? tern::launch_gemv(a) : tern::launch_gemm(a);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,15 +152,13 @@ tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *p
                              hipStream_t stream) {
     const tern_status st = check_matmul_args(X, x_dtype, packed_W, scales, 2, Y, y_dtype, M, N, K, group);
     if (st != TERN_OK) return st;
-    if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA)
-        return TERN_ERR_UNSUPPORTED;
-    if (path == TERN_PATH_GEMV && M > 0 && K > 0 && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
+    const tern_status pst = check_path(path, x_dtype, M, N, K);
+    if (pst != TERN_OK) return pst;
     if (M == 0 || N == 0) return TERN_OK;
     if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
 
     const tern::GemmArgs a = make_args(X, x_dtype, packed_W, scales, nullptr, nullptr, Y, y_dtype, M, N, K, stream);
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, N, K));
-    return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
+    return from_hip(dispatch(a, path));
 }
 
 tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed_W, const uint16_t *scales,
@@ -165,16 +187,14 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
     if (st != TERN_OK) return st;
     if (M > 0 && N > 0 && K > 0 && row_factor == nullptr) return TERN_ERR_NULL;
     if (!aligned(row_factor, 4)) return TERN_ERR_ALIGN;
-    if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA)
-        return TERN_ERR_UNSUPPORTED;
-    if (path == TERN_PATH_GEMV && M > 0 && K > 0 && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
+    const tern_status pst = check_path(path, x_dtype, M, N, K);
+    if (pst != TERN_OK) return pst;
     if (M == 0 || N == 0) return TERN_OK;
     if (K == 0) return from_hip(tern::launch_fill_zero(Y, M * N * (int64_t)dtype_size(y_dtype), stream));
 
     const tern::GemmArgs a =
         make_args(X, x_dtype, packed_W, nullptr, scales_q, row_factor, Y, y_dtype, M, N, K, stream);
-    const bool use_gemv = path == TERN_PATH_GEMV || (path == TERN_PATH_AUTO && auto_gemv(M, N, K));
-    return from_hip(use_gemv ? tern::launch_gemv(a) : tern::launch_gemm(a));
+    return from_hip(dispatch(a, path));
 }
 
 tern_status tern_block_map(const uint8_t *packed, uint32_t *block_map, int64_t N, int64_t K, int32_t group,

@@ -30,6 +30,17 @@ size_t gemv_lds_bytes(int64_t M, int64_t K);
 // N >= 12288).
 bool gemv_short(int64_t M, int64_t N, int64_t K);
 
+// Decode-path kernel with matrix-core sign selects, 1 <= M <= 4: weights
+// decoded to +-2 / 0 operands of v_mfma_f32_4x4x4_16b.  fits() is false when
+// the activations of the call do not fit the workgroup's LDS.
+bool gemv_mfma_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_mfma(const GemmArgs &a);
+
+// Decode-path kernel with 4-bit weight operands on the matrix cores (bf16
+// activations split exactly into two e4m3 terms), 1 <= M <= 4.
+bool gemv_fp4_fits(int64_t M, int64_t N, int64_t K, int x_dtype);
+hipError_t launch_gemv_fp4(const GemmArgs &a);
+
 // Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 2).
 hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map);
 size_t gemv_skip_lds_bytes(int64_t M, int64_t K);

@@ -46,6 +46,15 @@ def run(p, path="auto", tensors=None):
     return y
 
 
+def run_s8(x, w, q, r, M, N, y_dtype, path="auto"):
+    """tern_matmul_s8 into an output filled with NaN first (as run() does)."""
+    import ternary_weight_matmul_amd as tern
+    y = torch.full((M, N), float("nan"), dtype=TORCH_DT[y_dtype], device=x.device)
+    tern.matmul_s8_into(x, w, q, r, y, path=path)
+    torch.cuda.synchronize()
+    return y
+
+
 def check(y_bits: np.ndarray, y_dtype: str, Y: np.ndarray, B: np.ndarray, what: str = "") -> float:
     """Assert the pass criterion elementwise; return the worst error / allowance."""
     o = oracle.default()

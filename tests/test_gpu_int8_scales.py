@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import workloads  # noqa: E402
 from gpu_util import (TORCH_DT, bits_to_device, check, device, out_bits, problem_to_device,  # noqa: E402
-                      sample_indices)
+                      run_s8, sample_indices)
 
 tern = pytest.importorskip("ternary_weight_matmul_amd")
 
@@ -50,9 +50,8 @@ def test_quantize_bit_exact(N, G):
 
 def _run_s8(p, q, r, path):
     x, w, _ = problem_to_device(p)
-    y = tern.matmul_s8(x, w, torch.from_numpy(q).to(device()), torch.from_numpy(r).to(device()),
-                       out_dtype=TORCH_DT[p.y_dtype], path=path)
-    torch.cuda.synchronize()
+    y = run_s8(x, w, torch.from_numpy(q).to(device()), torch.from_numpy(r).to(device()),
+               p.shape.M, p.shape.N, p.y_dtype, path)
     return out_bits(y, p.y_dtype)
 
 
@@ -63,7 +62,9 @@ RAGGED = [(1, 128, 1), (1, 640, 33), (3, 1152, 50), (4, 3200, 29), (1, 17408, 5)
           # M <= 2, K and N <= 5120: the short-step decode kernel at each row count
           (1, 4992, 1025), (1, 2048, 2100), (1, 5120, 3071), (1, 1152, 5120), (2, 5120, 4097), (2, 640, 33),
           # M = 4 with one wave per workgroup: 80 outputs for 64 threads
-          (4, 384, 4500), (3, 5120, 2000), (4, 8192, 1500), (2, 7296, 700)]
+          (4, 384, 4500), (3, 5120, 2000), (4, 8192, 1500), (2, 7296, 700),
+          # M = 2 on layers of 12288 rows or more (several rounds of short-step workgroups)
+          (2, 5120, 12289), (2, 8192, 17408)]
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
@@ -73,7 +74,7 @@ def test_matmul_s8_ragged(M, K, N, xd, yd):
     p.scales = _scales(M + K + N, N, K // 128, zero_rows=(N - 1,) if N > 2 else ())
     q, r = O().quantize_scales(p.scales)
     Y, B = O().matmul_s8(p.x, xd, p.packed, q, r, M, N, K, threads=8)
-    for path in ["auto", "mfma"] + (["gemv"] if M <= tern.GEMV_MAX_M else []):
+    for path in ["auto", "mfma"] + (["gemv", "gemv_mfma"] if M <= tern.GEMV_MAX_M else []):
         check(_run_s8(p, q, r, path), yd, Y, B, f"{M}x{K}x{N} {path}")
 
 
@@ -107,11 +108,11 @@ def test_matmul_s8_exact_bit_exact(M, K, N, xd):
     q = rng.integers(-127, 128, (N, K // 128)).astype(np.int8)
     r = (2.0 ** rng.integers(-12, -6, N)).astype(np.float32)
     Y, _ = O().matmul_s8(xbits, xd, P, q, r, M, N, K)
-    paths = (("gemv", "f32"), ("mfma", "f32"), ("gemv", "bf16"), ("mfma", "bf16"))
+    paths = (("gemv", "f32"), ("mfma", "f32"), ("gemv", "bf16"), ("mfma", "bf16"), ("gemv_mfma", "f32"),
+             ("gemv_mfma", "bf16"))
     for path, yd in paths if M <= tern.GEMV_MAX_M else [pp for pp in paths if pp[0] == "mfma"]:
-        y = tern.matmul_s8(bits_to_device(xbits, xd), torch.from_numpy(P).to(device()),
-                           torch.from_numpy(q).to(device()), torch.from_numpy(r).to(device()),
-                           out_dtype=TORCH_DT[yd], path=path)
+        y = run_s8(bits_to_device(xbits, xd), torch.from_numpy(P).to(device()),
+                   torch.from_numpy(q).to(device()), torch.from_numpy(r).to(device()), M, N, yd, path)
         got = O().decode(out_bits(y, yd), yd)
         assert np.array_equal(got, O().round(Y, yd)), (path, yd)
 
@@ -121,8 +122,7 @@ def test_quantized_scales_feed_the_product():
     p = workloads.make_custom(123, 2, 5120, 300, x_dtype="bf16", y_dtype="f32")
     x, w, s = problem_to_device(p)
     dq, dr = tern.quantize_scales(s)
-    y = tern.matmul_s8(x, w, dq, dr, out_dtype=torch.float32)
-    torch.cuda.synchronize()
+    y = run_s8(x, w, dq, dr, 2, 300, "f32")
     q, r = O().quantize_scales(p.scales)
     Y, B = O().matmul_s8(p.x, "bf16", p.packed, q, r, 2, 300, 5120, threads=8)
     check(out_bits(y, "f32"), "f32", Y, B, "quantised chain")
