@@ -56,8 +56,10 @@ typedef enum { TERN_F16 = 0, TERN_BF16 = 1, TERN_F32 = 2 } tern_dtype;
 
 /* Which kernel family computes tern_matmul_path's result. */
 typedef enum {
-    TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): GEMV for M <= 2, and for
-                           M <= 4 with N <= 5120 and K <= 8192; else MFMA */
+    TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): for M <= 4, GEMV_FP4 with
+                           bf16 X (K <= 32768), else with fp16 X GEMV_MFMA for M = 3, 4 where
+                           it fits and GEMV for M <= 2 or where GEMV_MFMA does not fit;
+                           MFMA for every other shape */
     TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
     TERN_PATH_MFMA = 2, /* LDS-staged activations + in-register weight decode + MFMA; any M */
     TERN_PATH_GEMV_MFMA = 3, /* decode kernel whose sign-select sums run on the matrix cores
@@ -66,7 +68,7 @@ typedef enum {
     TERN_PATH_GEMV_FP4 = 4  /* decode kernel with the weights as 4-bit (e2m1 +-2 / 0) matrix-core
                                operands and each bf16 activation split exactly into two e4m3
                                terms with a power-of-two scale per 32 (v_mfma_scale_f32_
-                               16x16x128_f8f6f4); bf16 X only, M <= 4, X staged whole in LDS */
+                               16x16x128_f8f6f4); bf16 X only, M <= 4, K <= 32768 */
 } tern_path;
 
 #define TERN_GROUP 128

@@ -90,6 +90,20 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K) {
     return (M <= kAutoGemvMaxM && gemv_fits(M, K)) || tern::gemv_short(M, N, K);
 }
 
+// With bf16 activations the fp4 matrix-core decode kernel is the fastest of
+// the decode kernels at every M <= 4 measured (graph-timed, weights rotated
+// over 2 GB; M = 1: 5120 -> 5120 4.04 us against the VALU kernel's 4.16,
+// 5120 -> 17408 7.34 against 8.28, 17408 -> 5120 8.51 against 9.08; M = 4:
+// 5120 -> 17408 11.0 against 29.4 (VALU) and 13.4 (16-row MFMA tiles),
+// 17408 -> 5120 12.7 against 23.9 and 15.9).  With fp16 activations the
+// 4x4x4 matrix-core kernel takes M = 3, 4 (M = 4: 5120 -> 17408 11.3 us
+// against 13.4, 5120 -> 5120 6.1 against the VALU kernel's 6.5).
+tern_path auto_path(const tern::GemmArgs &a) {
+    if (a.M <= 4 && a.x_dtype == 1 && tern::gemv_fp4_fits(a.M, a.N, a.K, 1)) return TERN_PATH_GEMV_FP4;
+    if (a.M >= 3 && a.M <= 4 && a.x_dtype == 0 && tern::gemv_mfma_fits(a.M, a.N, a.K)) return TERN_PATH_GEMV_MFMA;
+    return auto_gemv(a.M, a.N, a.K) ? TERN_PATH_GEMV : TERN_PATH_MFMA;
+}
+
 // A forced path that cannot run this shape is TERN_ERR_UNSUPPORTED (checked
 // before anything is launched).
 tern_status check_path(tern_path path, tern_dtype x_dtype, int64_t M, int64_t N, int64_t K) {
@@ -110,7 +124,10 @@ hipError_t dispatch(const tern::GemmArgs &a, tern_path path) {
     case TERN_PATH_MFMA: return tern::launch_gemm(a);
     case TERN_PATH_GEMV_MFMA: return tern::launch_gemv_mfma(a);
     case TERN_PATH_GEMV_FP4: return tern::launch_gemv_fp4(a);
-    default: return auto_gemv(a.M, a.N, a.K) ? tern::launch_gemv(a) : tern::launch_gemm(a);
+    default: {
+        const tern_path p = auto_path(a);
+        return p == TERN_PATH_AUTO ? hipErrorInvalidValue : dispatch(a, p);
+    }
     }
 }
 

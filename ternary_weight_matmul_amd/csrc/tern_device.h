@@ -38,34 +38,50 @@ __device__ __forceinline__ uint32_t sign_nz_fields(uint32_t w) {
 // 64-bit shifts of a register pair.  On gfx950 v_lshlrev_b64 issues at the
 // same rate as a 32-bit shift, so one instruction moves the fields of two
 // code words; the compiler would split it into two 32-bit operations.
-template <int S>
+//
+// MC = true (kernels that issue matrix-core instructions) takes the plain C++
+// shift instead.  The inline-asm form hides the instruction from the
+// compiler's hazard recognizer, which then does not keep it away from an
+// MFMA still in flight: an MFMA writes its result registers many cycles
+// after it issues, and the register allocator may hand a result register
+// the program never reads (an unused D row) to the asm output, which the
+// MFMA then overwrites.  Measured on the fp4 decode kernel: the even-weight
+// nibbles of one operand, written by the asm shift three instructions after
+// an MFMA whose unused D rows shared their registers, came out zero.
+template <int S, bool MC = false>
 __device__ __forceinline__ uint64_t shl64(uint64_t v) {
-    if constexpr (S == 0) {
-        return v;
+    if constexpr (S == 0 || MC) {
+        return v << S;
     } else {
         uint64_t r;
         asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(v));
         return r;
     }
 }
+template <bool MC = false>
 __device__ __forceinline__ uint64_t shr64_1(uint64_t v) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, 1, %1" : "=v"(r) : "v"(v));
-    return r;
+    if constexpr (MC) {
+        return v >> 1;
+    } else {
+        uint64_t r;
+        asm("v_lshrrev_b64 %0, 1, %1" : "=v"(r) : "v"(v));
+        return r;
+    }
 }
 
 // Field transform of two code words at once (bits that cross between the
 // words are cleared by the 0x5555... mask).
+template <bool MC = false>
 __device__ __forceinline__ uint64_t sign_nz_fields64(uint64_t w) {
-    return w ^ (shr64_1(w) & 0x5555555555555555ull);
+    return w ^ (shr64_1<MC>(w) & 0x5555555555555555ull);
 }
 
 // +-2 / 0 pairs for weights (i, i+8) of both words of a transformed pair:
 // after a 64-bit shift by 14 - 2i, the bits that cross from the low word
 // into the high word land below bit 14 and are masked away.
-template <int I>
+template <int I, bool MC = false>
 __device__ __forceinline__ void weight_pairs2(uint64_t v, uint32_t &lo, uint32_t &hi) {
-    const uint64_t t = shl64<14 - 2 * I>(v);
+    const uint64_t t = shl64<14 - 2 * I, MC>(v);
     lo = (uint32_t)t & 0xC000C000u;
     hi = (uint32_t)(t >> 32) & 0xC000C000u;
 }
@@ -80,10 +96,10 @@ __device__ __forceinline__ uint32_t half_masks(uint32_t u) {
 // pair, s2 = the scale's bits in both halves: s with the code's sign where the
 // field is nonzero, +0 where it is zero (codes 00 and 11).  No arithmetic, so
 // every finite scale gives its exact product.
-template <int I>
+template <int I, bool MC = false>
 __device__ __forceinline__ void scaled_pairs2(uint64_t v, uint32_t s2, uint32_t &lo, uint32_t &hi) {
-    const uint64_t t = shl64<14 - 2 * I>(v);   // signs at bits 15, 31 (and 47, 63)
-    const uint64_t u = shl64<15 - 2 * I>(v);   // nonzero flags at bits 15, 31 (and 47, 63)
+    const uint64_t t = shl64<14 - 2 * I, MC>(v);   // signs at bits 15, 31 (and 47, 63)
+    const uint64_t u = shl64<15 - 2 * I, MC>(v);   // nonzero flags at bits 15, 31 (and 47, 63)
     lo = (((uint32_t)t & 0x80008000u) ^ s2) & half_masks((uint32_t)u);
     hi = (((uint32_t)(t >> 32) & 0x80008000u) ^ s2) & half_masks((uint32_t)(u >> 32));
 }

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * WN * WK, TWO ? 8 : 1) void gemm_kernel(const u
                 if constexpr (CT)
                     wv = *reinterpret_cast<const uint2 *>(c_lds + buf * BN * 256 +
                                                           c_piece_off(16 * (NB * wn + nb) + li, wk * 4 + lg));
-                v[nb] = sign_nz_fields64((uint64_t)wv.x | ((uint64_t)wv.y << 32));
+                v[nb] = sign_nz_fields64<true>((uint64_t)wv.x | ((uint64_t)wv.y << 32));
             }
 
             float4_t part[MB][NB];
@@ -260,10 +260,10 @@ __global__ __launch_bounds__(64 * WN * WK, TWO ? 8 : 1) void gemm_kernel(const u
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     uint32_t lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
-                    weight_pairs2<4 * H + 0>(v[nb], lo0, hi0);
-                    weight_pairs2<4 * H + 1>(v[nb], lo1, hi1);
-                    weight_pairs2<4 * H + 2>(v[nb], lo2, hi2);
-                    weight_pairs2<4 * H + 3>(v[nb], lo3, hi3);
+                    weight_pairs2<4 * H + 0, true>(v[nb], lo0, hi0);
+                    weight_pairs2<4 * H + 1, true>(v[nb], lo1, hi1);
+                    weight_pairs2<4 * H + 2, true>(v[nb], lo2, hi2);
+                    weight_pairs2<4 * H + 3, true>(v[nb], lo3, hi3);
                     blo[nb] = make_uint4(lo0, lo1, lo2, lo3);
                     bhi[nb] = make_uint4(hi0, hi1, hi2, hi3);
                 }

@@ -146,21 +146,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_big_kernel(const uint1
     };
     auto store_w = [&](int buf, uint2 wc, uint32_t sb) {
         if (w_role) {
-            const uint64_t v = sign_nz_fields64((uint64_t)wc.x | ((uint64_t)wc.y << 32));
+            const uint64_t v = sign_nz_fields64<true>((uint64_t)wc.x | ((uint64_t)wc.y << 32));
             // S8: the block's int8 code q as an fp16 value (exact: |q| <= 127);
             // the row factor multiplies the finished sums in the epilogue
             const uint32_t sh = S8 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int32_t)sb) : sb;
             const uint32_t s2 = sh | (sh << 16);
             // products of weights (i, i+8) of code word 0 (a*) and word 1 (b*)
             uint32_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
-            scaled_pairs2<0>(v, s2, a0, b0);
-            scaled_pairs2<1>(v, s2, a1, b1);
-            scaled_pairs2<2>(v, s2, a2, b2);
-            scaled_pairs2<3>(v, s2, a3, b3);
-            scaled_pairs2<4>(v, s2, a4, b4);
-            scaled_pairs2<5>(v, s2, a5, b5);
-            scaled_pairs2<6>(v, s2, a6, b6);
-            scaled_pairs2<7>(v, s2, a7, b7);
+            scaled_pairs2<0, true>(v, s2, a0, b0);
+            scaled_pairs2<1, true>(v, s2, a1, b1);
+            scaled_pairs2<2, true>(v, s2, a2, b2);
+            scaled_pairs2<3, true>(v, s2, a3, b3);
+            scaled_pairs2<4, true>(v, s2, a4, b4);
+            scaled_pairs2<5, true>(v, s2, a5, b5);
+            scaled_pairs2<6, true>(v, s2, a6, b6);
+            scaled_pairs2<7, true>(v, s2, a7, b7);
             uint8_t *w_t = lds + 2 * A_TILE + buf * W_TILE;
             // natural order: chunk 4h = weights 0..7 of word 0, 4h+1 = 8..15, 4h+2/3 from word 1
             *reinterpret_cast<uint4 *>(w_t + w_dst0) =

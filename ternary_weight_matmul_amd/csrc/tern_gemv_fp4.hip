@@ -40,22 +40,29 @@
 // (bytes 16..31), evens first, then odds.
 //
 // Work layout.
-//   * unit = (quad q, step s): rows 4q..4q+3 x 512 weights (4 blocks g0..g0+3,
-//     g0 = 4s).  B column j = 4r + c is (row 4q + r, block g0 + c); lane l
-//     loads the 8 code bytes of slice l/16 of its column (each row's 16 lanes
-//     read 128 contiguous bytes).  A row i = 4c + 2h + m (M <= 2: one MFMA,
-//     term h and row m both in it) or i = 4c + m (M = 3, 4: one MFMA per
-//     term): only D entries with A block c = B block c are used -- lanes l
-//     with l/16 = l%4, VGPR 2h + m (or m).
-//   * one workgroup of 16 waves per CU takes a contiguous range of quads;
-//     units are numbered quad-major; wave w takes units [UPW w, UPW w + UPW);
-//   * all waves first split and stage the workgroup's activations in LDS,
-//     with every code and scale load of the wave already issued behind them;
-//   * per unit: 1 or 2 MFMAs, acc += s * (D_hi + D_lo) on the 16 lanes that
-//     hold same-block entries; when the wave leaves a quad these write their
-//     sums to LDS; after a barrier each output adds its 4 blocks' and waves'
-//     partials in a fixed order (deterministic), halves the sum (the weights
-//     are +-2) and rounds it to the output type.
+//   * B column j = 4 r + c is (row r of a 4-row quad, block c of a 512-weight
+//     step): lane (p, j) loads the 8 code bytes of slice p of that block, so
+//     one load instruction reads 4 rows x 128 contiguous bytes (whole cache
+//     lines; measured: loads that cover only half of each row's line, as in
+//     a 16-row x 64-byte pattern, stream 25-50% slower).  A row i = 4 c' +
+//     2 h + m (M <= 2: one MFMA, term h and row m in it) or 4 c' + m (M = 3,
+//     4: one MFMA per term, chained) carries the activations of block c', so
+//     only the entries with c' = c are used: lanes with p = c, VGPR 2 h + m
+//     (or m).  Each such lane multiplies them by the scale of its own (row,
+//     block) and keeps a running sum.
+//   * A workgroup takes Q quads (4 Q rows) and all of K; its waves split K
+//     into 512-weight steps, SPW consecutive steps per wave, and each wave
+//     loops over the Q quads of its steps with every code and scale load
+//     issued at the start.
+//   * Each wave splits and stages only its own steps' activations into a
+//     wave-private LDS area laid out as the A registers (8 M images of 4
+//     lanes x 32 bytes per step, then their block-scale bytes): no
+//     workgroup barrier before the products, and one step's A registers
+//     serve all Q quads.
+//   * At the end the used lanes write their sums to LDS and after one
+//     barrier each output adds its 4 blocks and the waves in a fixed order
+//     (deterministic), halves the sum (the weights are +-2) and rounds it to
+//     the output type.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,11 +75,10 @@ namespace tern {
 
 namespace {
 
-constexpr int F_STEP = 512;          // weights of a row per unit
-constexpr int F_BPU = F_STEP / 128;  // 128-weight blocks per unit (4)
-constexpr int F_WAVES = 16;
-constexpr int F_THREADS = 64 * F_WAVES;
-constexpr int F_MAX_UPW = 12;
+constexpr int F_STEP = 512;          // weights of a row per step
+constexpr int F_MAX_WAVES = 16;
+constexpr int F_MAX_SPW = 4;
+constexpr int F_IMG = 128;           // one A image: 4 lanes x 32 bytes
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -90,14 +96,6 @@ __device__ __forceinline__ uint32_t opaque_lanes(bool c) {
     asm("" : "+v"(m));
     return m;
 }
-
-// A block (128 bytes: 4 slices of 32) of activation row m, term h (0 = hi,
-// 1 = lo), weight block g: index k = (2 g + h) M + m.  Slice p sits at
-// 32 ((p + (k >> 1)) & 3) inside the block, which spreads the A reads of the
-// 16 lanes of one slice over the banks; for a lane the rotation does not
-// depend on the unit (the blocks of a unit start at a multiple of 4).
-__device__ __forceinline__ int ablock(int M, int g, int h, int m) { return (2 * g + h) * M + m; }
-__device__ __forceinline__ int aslice(int k, int p) { return k * 128 + 32 * ((p + (k >> 1)) & 3); }
 
 // Largest of the 8 bf16 magnitudes in q (as integers: same order as values).
 __device__ __forceinline__ uint32_t max_mag8(const uint4 &q) {
@@ -150,237 +148,216 @@ __device__ __forceinline__ void split8(const uint4 &q, uint32_t eh, uint32_t el,
     lo_odd = __builtin_amdgcn_perm(lb23, lb01, 0x07050301u);
 }
 
-// D = A * B on the matrix cores: A e4m3 with per-lane block scale sa (E8M0),
-// B e2m1 (scale 1).
-__device__ __forceinline__ float4_t mfma_f8f4(const uint4 &a0, const uint4 &a1, const uint4 &b, uint32_t sa) {
-    const int8v_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+// D = A * B + C on the matrix cores: A e4m3 with per-lane block scale sa
+// (E8M0), B e2m1 (scale 1).
+__device__ __forceinline__ float4_t mfma_f8f4(const int8v_t &av, const uint4 &b, const float4_t &c, uint32_t sa) {
     const int8v_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-    const float4_t z = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 0 /* A e4m3 */, 4 /* B e2m1 */, 0,
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0 /* A e4m3 */, 4 /* B e2m1 */, 0,
                                                             (int)sa, 0, 127);
 }
 
-// UPW: units per wave; OPT: 8-activation octets staged per thread.
-template <int M, bool S8, int UPW, int OPT>
-__global__ __launch_bounds__(F_THREADS) void gemv_fp4_kernel(const uint16_t *__restrict__ X,
-                                                             const uint8_t *__restrict__ P,
-                                                             const uint16_t *__restrict__ S,
-                                                             const int8_t *__restrict__ Q,
-                                                             const float *__restrict__ R, void *__restrict__ Y,
-                                                             int y_dtype, int N, int K, int nquads, int kmax) {
-    constexpr int TERMS_PER_MFMA = M <= 2 ? 2 : 1;   // hi and lo rows in one MFMA, or one MFMA per term
+// 8 code bytes -> 32 e2m1 weights (+-2 / 0) in the K order of the header.
+__device__ __forceinline__ uint4 fp4_weights(uint32_t w0, uint32_t w1) {
+    const uint64_t v = sign_nz_fields64<true>((uint64_t)w0 | ((uint64_t)w1 << 32));
+    const uint64_t e = shl64<2, true>(v);
+    return make_uint4((uint32_t)e & 0xCCCCCCCCu, (uint32_t)v & 0xCCCCCCCCu, (uint32_t)(e >> 32) & 0xCCCCCCCCu,
+                      (uint32_t)(v >> 32) & 0xCCCCCCCCu);
+}
+
+// (steps per wave, quads per workgroup) pairs that are instantiated.
+#define TERN_F4_TABLE(X)                                                                                       \
+    X(1, 1) X(1, 2) X(1, 3) X(1, 4) X(1, 5) X(1, 6) X(1, 8) X(1, 10) X(1, 12) X(1, 17) X(2, 1) X(2, 2) X(2, 3) \
+    X(2, 4) X(2, 5) X(2, 6) X(2, 8) X(3, 1) X(3, 2) X(3, 3) X(3, 4) X(3, 5) X(4, 1) X(4, 2) X(4, 3) X(4, 4)
+
+// LDS bytes of one wave's step: 8 M A images, then their scale bytes.
+template <int M>
+constexpr int step_lds() {
+    return 8 * M * (F_IMG + 4);
+}
+
+template <int M, bool S8, int Q, int SPW>
+__global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16_t *__restrict__ X,
+                                                                  const uint8_t *__restrict__ P,
+                                                                  const uint16_t *__restrict__ S,
+                                                                  const int8_t *__restrict__ Qs,
+                                                                  const float *__restrict__ Rf, void *__restrict__ Y,
+                                                                  int y_dtype, int N, int K) {
+    constexpr int IMGS = 8 * M;
+    constexpr int SL = step_lds<M>();
+    constexpr bool ONE = M <= 2;   // hi and lo terms in one MFMA
     extern __shared__ uint4 lds[];
     char *ldsb = reinterpret_cast<char *>(lds);
-    const int groups = K >> 7;
-    const int steps = (groups + F_BPU - 1) / F_BPU;
-    const int g4 = steps * F_BPU;                    // blocks staged (zero padded to whole units)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;
     const int p = lane >> 4;        // K slice of the lane (A and B)
     const int col = lane & 15;      // B column: 4 r + c
-    const int r = col >> 2;         // weight row within the quad
-    const int c = col & 3;          // weight block within the unit
-    const int G = gridDim.x;
-    const int qa = (int)((int64_t)blockIdx.x * nquads / G);
-    const int qb = (int)((int64_t)(blockIdx.x + 1) * nquads / G);
-    const int U = (qb - qa) * steps;
-    const int ufirst = wave * UPW;
-    const int64_t row_bytes = K >> 2;
-    const int abytes = M * 2 * g4 * 128;             // staged activations
-    const int sbytes_lds = M * 2 * g4 * 4;           // their block scales (E8M0)
-    char *ascale = ldsb + abytes;
-    float4_t *red = reinterpret_cast<float4_t *>(ldsb + abytes + sbytes_lds);   // [F_WAVES][kmax][16 (r, c)], then 64 lane spares
+    const int r = col >> 2;
+    const int c = col & 3;
+    const int steps = (K + F_STEP - 1) / F_STEP;
+    const int groups = K >> 7;
+    const int row_bytes = K >> 2;
+    const int n0 = blockIdx.x * 4 * Q;
+    const int rows = min(4 * Q, N - n0);
+    char *wimg = ldsb + wave * SL;   // one step's images, reused step after step
+    float *red = reinterpret_cast<float *>(ldsb + nw * SL);   // [nw][Q][16][M], then [64][M] spares
+    float *spare = red + nw * Q * 16 * M;
+    char *spare_byte = reinterpret_cast<char *>(spare + 64 * M);
 
-    // ---- 1. loads: activation octets first, then every code and scale load
-    //         of the wave (buffer loads rebased per unit on the scalar unit;
-    //         rows past N read zeros; blocks past K read finite bytes that meet
-    //         zero activations) ----
-    const int octs = M * g4 * 16;                    // 8-activation octets, padding included
-    uint4 xq[OPT];
+    // ---- 1. loads: this lane's activation octets first, then every code and
+    //         scale load of the wave (rows past N read zeros; bytes past K
+    //         meet zero activations, and their scales are dropped) ----
+    uint4 xq[SPW][M];
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) {
-        const int t = tid + i * F_THREADS;
-        const int m = min(t / (g4 * 16), M - 1);
-        const int o = t % (g4 * 16);                 // octet within the row
-        const int oc = min(o, (K >> 3) - 1);
-        xq[i] = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (int64_t)oc * 8);
+    for (int st = 0; st < SPW; ++st) {
+        const int k0 = min((wave * SPW + st) * F_STEP + 8 * lane, K - 8);
+#pragma unroll
+        for (int m = 0; m < M; ++m) xq[st][m] = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + k0);
     }
-    // keep the activation loads ahead of the code loads: the staging waits for them alone
     __builtin_amdgcn_sched_barrier(0);
-    const int wg_rows = min(4 * qb, N) - 4 * qa;
-    const uint8_t *Pwg = P + (int64_t)4 * qa * row_bytes;
-    const uint32_t pbytes = (uint32_t)(wg_rows * row_bytes);
     constexpr int SB = S8 ? 1 : 2;
-    const char *Swg = S8 ? reinterpret_cast<const char *>(Q + (int64_t)4 * qa * groups)
-                         : reinterpret_cast<const char *>(S + (int64_t)4 * qa * groups);
-    const uint32_t sbytes = (uint32_t)(wg_rows * groups * SB);
-    const int pofs = r * (int)row_bytes + c * 32 + p * 8;   // this lane's 8 code bytes within a unit
-    const int sofs = (r * groups + c) * SB;                // this lane's block scale within a unit
-    uint2 code[UPW];
-    uint32_t sbits[UPW];
+    const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+    const char *sbase = S8 ? reinterpret_cast<const char *>(Qs + (int64_t)n0 * groups)
+                           : reinterpret_cast<const char *>(S + (int64_t)n0 * groups);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sbase, (uint32_t)(rows * groups * SB));
+    uint2 code[SPW][Q];
+    uint32_t sbits[SPW][Q];
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        const int u = min(ufirst + i, U - 1);
-        const int ql = u / steps;
-        const int s = u - ql * steps;
-        const uint32_t pu = (uint32_t)(4 * ql * row_bytes + s * (F_STEP / 4));
-        const uint32_t su = (uint32_t)((4 * ql * groups + s * F_BPU) * SB);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(Pwg + pu, pbytes - pu), pofs, 0, 2 /* nt */));
-        code[i] = make_uint2(v[0], v[1]);
-        if constexpr (S8)
-            sbits[i] = (uint32_t)(int32_t)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(buffer_rsrc(Swg + su, sbytes - su),
-                                                                                     sofs, 0, 0);
-        else
-            sbits[i] = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(Swg + su, sbytes - su), sofs, 0, 0);
-    }
-
-    // ---- 2. split and stage the activations.  Octet o of block g (elements
-    //         128 g + 8 o ..) is quarter o % 4 of 32-block o / 4: the 4 lanes of
-    //         a DPP quad hold one 32-block and share its maximum.  Written
-    //         without branches (threads past the last octet write a spare
-    //         slot), so the activation loads stay ahead of the code loads. ----
-    const int spare = abytes + sbytes_lds + F_WAVES * kmax * 256 + 64 * 16;   // after the per-lane flush spares
+    for (int st = 0; st < SPW; ++st) {
+        const int s = min(wave * SPW + st, steps - 1);
+        const int blk = min(4 * s + c, groups - 1);
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) {
-        const int t = tid + i * F_THREADS;
-        const bool valid = t < octs;
-        const int m = min(t / (g4 * 16), M - 1);
-        const int o = t % (g4 * 16);
-        const int g = o >> 4;                        // 128-weight block
-        const int ob = o & 15;                       // octet within the block
-        uint4 q = xq[i];
-        const uint32_t keep = opaque_lanes(o < (K >> 3));   // zero padding past K
-        q.x &= keep;
-        q.y &= keep;
-        q.z &= keep;
-        q.w &= keep;
-        const uint32_t mx = quad_max(max_mag8(q));   // largest magnitude of the 32-block
-        const uint32_t eb = mx >> 7;                 // its biased exponent
-        const uint32_t eh = eb > 8 ? eb - 7 : 1;     // hi scale 2^(E - 7), at least 2^-126
-        const uint32_t el = eh > 5 ? eh - 4 : 1;     // lo scale 2^(E - 11)
-        uint32_t he, ho, le, lo;
-        split8(q, eh, el, he, ho, le, lo);
-        // the 16-element chunk ob / 2 of the block goes to A slice (ob / 2) % 4,
-        // half (ob / 2) / 4; this octet is half ob % 2 of the chunk's evens and odds
-        const int ch = ob >> 1;
-        const int sl = ch & 3;
-        const int off = 16 * (ch >> 2) + 4 * (ob & 1);
-        const int kh = ablock(M, g, 0, m), kl = ablock(M, g, 1, m);
-        const int ah = valid ? aslice(kh, sl) + off : spare;
-        const int al = valid ? aslice(kl, sl) + off : spare + 16;
-        *reinterpret_cast<uint32_t *>(ldsb + ah) = he;
-        *reinterpret_cast<uint32_t *>(ldsb + ah + 8) = ho;
-        *reinterpret_cast<uint32_t *>(ldsb + al) = le;
-        *reinterpret_cast<uint32_t *>(ldsb + al + 8) = lo;
-        // block scales: A scale of slice p covers weights 32p..32p+31 of the block
-        if ((ob & 3) == 0) {
-            const int sb = ob >> 2;
-            ascale[valid ? kh * 4 + sb : sbytes_lds] = (char)eh;
-            ascale[valid ? kl * 4 + sb : sbytes_lds] = (char)el;
+        for (int q = 0; q < Q; ++q) {
+            const int off = (4 * q + r) * row_bytes + s * (F_STEP / 4) + c * 32 + p * 8;
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, 2 /* nt */));
+            code[st][q] = make_uint2(v[0], v[1]);
+            const int soff = ((4 * q + r) * groups + blk) * SB;
+            if constexpr (S8)
+                sbits[st][q] = (uint32_t)(int32_t)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, 0);
+            else
+                sbits[st][q] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0);
         }
     }
+
+    // ---- 2. per step: split the wave's activations and stage them as A
+    //         images, then read this lane's A registers and run the quads.
+    //         Staging: lane t holds octet t of the step: block g = t / 16,
+    //         32-run u = (t / 4) % 4 of the block (its weights 32 u .. 32 u +
+    //         31, the K slots of B lane group u), octet o = t % 4 of the run.
+    //         Run u's 32 slots are A lanes 2 (u % 2) and 2 (u % 2) + 1, bytes
+    //         16 (u / 2) .. +15: the octet's evens at byte 4 (o % 2) of lane
+    //         2 (u % 2) + o / 2, its odds 8 bytes further.  The run's scale is
+    //         byte u of the image's scale word.  A DPP quad holds one run.
+    //         Products: A lane (p, i) takes image (c', h, m) of its row i, the
+    //         32 bytes of lane p; rows m >= M read as zeros. ----
+    const int sg = lane >> 4;
+    const int su = (lane >> 2) & 3;
+    const int so = lane & 3;
+    const int loff = (2 * (su & 1) + (so >> 1)) * 32 + 16 * (su >> 1) + 4 * (so & 1);
+    const int ca = col >> 2;                       // A block of the lane's row
+    const int ha = ONE ? (col >> 1) & 1 : 0;
+    const int ma = ONE ? (col & 1) : (col & 3);
+    const uint32_t arow = opaque_lanes(ma < M);
+    const int mc = min(ma, M - 1);
+    float acc[Q][M];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[q][m] = 0.f;
+#pragma unroll
+    for (int st = 0; st < SPW; ++st) {
+        const int s = wave * SPW + st;
+        if (SPW > 1 && s >= steps) break;   // wave-uniform
+        if (st > 0) {
+            // the previous step's A reads are done before its images are overwritten
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        const uint32_t keep = opaque_lanes(s * F_STEP + 8 * lane < K);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            uint4 xv = xq[st][m];
+            xv.x &= keep;
+            xv.y &= keep;
+            xv.z &= keep;
+            xv.w &= keep;
+            const uint32_t mx = quad_max(max_mag8(xv));  // largest magnitude of the 32-run
+            const uint32_t eb = mx >> 7;                 // its biased exponent
+            const uint32_t eh = eb > 8 ? eb - 7 : 1;     // hi scale 2^(E - 7), at least 2^-126
+            const uint32_t el = eh > 5 ? eh - 4 : 1;     // lo scale 2^(E - 11)
+            uint32_t he, ho, le, lo;
+            split8(xv, eh, el, he, ho, le, lo);
+            const int ih = (sg * 2 + 0) * M + m;
+            const int il = (sg * 2 + 1) * M + m;
+            *reinterpret_cast<uint32_t *>(wimg + ih * F_IMG + loff) = he;
+            *reinterpret_cast<uint32_t *>(wimg + ih * F_IMG + loff + 8) = ho;
+            *reinterpret_cast<uint32_t *>(wimg + il * F_IMG + loff) = le;
+            *reinterpret_cast<uint32_t *>(wimg + il * F_IMG + loff + 8) = lo;
+            // one lane of the quad writes the run's scale bytes (the others a
+            // spare byte: no branch around the stores)
+            *(so == 0 ? wimg + IMGS * F_IMG + ih * 4 + su : spare_byte) = (char)eh;
+            *(so == 0 ? wimg + IMGS * F_IMG + il * 4 + su : spare_byte) = (char)el;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        int8v_t a[2];
+        uint32_t sa[2];
+#pragma unroll
+        for (int h = 0; h < (ONE ? 1 : 2); ++h) {
+            const int img = (ca * 2 + (ONE ? ha : h)) * M + mc;
+            const uint4 d0 = *reinterpret_cast<const uint4 *>(wimg + img * F_IMG + p * 32);
+            const uint4 d1 = *reinterpret_cast<const uint4 *>(wimg + img * F_IMG + p * 32 + 16);
+            a[h] = (int8v_t){(int)(d0.x & arow), (int)(d0.y & arow), (int)(d0.z & arow), (int)(d0.w & arow),
+                             (int)(d1.x & arow), (int)(d1.y & arow), (int)(d1.z & arow), (int)(d1.w & arow)};
+            sa[h] = (unsigned char)wimg[IMGS * F_IMG + img * 4 + p];
+        }
+        const bool blk_ok = 4 * s + c < groups;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const float4_t z = {0.f, 0.f, 0.f, 0.f};
+            const uint4 bw = fp4_weights(code[st][q].x, code[st][q].y);
+            float4_t d = mfma_f8f4(a[0], bw, z, sa[0]);
+            if constexpr (!ONE) d = mfma_f8f4(a[1], bw, d, sa[1]);
+            float sc = S8 ? (float)(int32_t)sbits[st][q] : f16_bits_to_float((uint16_t)sbits[st][q]);
+            sc = blk_ok ? sc : 0.f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[q][m] = fmaf(sc, ONE ? d[m] + d[2 + m] : d[m], acc[q][m]);
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < SPW; ++st)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) asm volatile("" ::"v"(code[st][q].x), "v"(sbits[st][q]));
+
+    // ---- 4. the lanes with p = c hold the used sums: they write them (the
+    //         others into spares, so every lane stores and no MFMA sits under
+    //         a partial EXEC mask), then each output adds its 4 blocks and the
+    //         waves in order ----
+    const bool holder = p == c;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            *(holder ? red + ((wave * Q + q) * 16 + col) * M + m : spare + lane * M + m) = acc[q][m];
     __syncthreads();
-
-    // ---- 3. units ----
-    // A row of this lane: M <= 2: i = 4 ci + 2 h + m; M = 3, 4: i = 4 ci + m
-    // (ci is the A block, the lane's row within the MFMA is col = lane & 15)
-    const int ci = col >> 2;
-    int ka[2];
-    if constexpr (M <= 2) {
-        const int h = (col >> 1) & 1;
-        const int m = min(col & 1, M - 1);
-        ka[0] = ablock(M, ci, h, m);
-        ka[1] = ka[0];
-    } else {
-        const int m = min(col & 3, M - 1);
-        ka[0] = ablock(M, ci, 0, m);
-        ka[1] = ablock(M, ci, 1, m);
-    }
-    const char *abase0 = ldsb + aslice(ka[0], p);
-    const char *abase1 = ldsb + aslice(ka[1], p);
-    const unsigned char *sbase0 = reinterpret_cast<const unsigned char *>(ascale) + ka[0] * 4 + p;
-    const unsigned char *sbase1 = reinterpret_cast<const unsigned char *>(ascale) + ka[1] * 4 + p;
-    const int ustride_a = F_BPU * 2 * M * 128;       // A bytes per unit step
-    const int ustride_s = F_BPU * 2 * M * 4;
-    const bool holder = p == c;                      // lane holds same-block D entries
-    float acc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.f;
-    const int u0 = min(ufirst, U - 1);
-    const int qfirst = u0 / steps;
-    int ql = qfirst;
-    int s = u0 - qfirst * steps;
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        const int u = ufirst + i;
-        if (i > 0) {
-            if (++s == steps) {
-                s = 0;
-                ++ql;
-            }
-        }
-        if (u < U) {
-            // decode: 32 fp4 weights, K order 32p + 8d + t <-> weight 16 (d/2) + 2t + (d%2)
-            const uint64_t v = sign_nz_fields64((uint64_t)code[i].x | ((uint64_t)code[i].y << 32));
-            const uint64_t e = shl64<2>(v);
-            const uint4 bw = make_uint4((uint32_t)e & 0xCCCCCCCCu, (uint32_t)v & 0xCCCCCCCCu,
-                                        (uint32_t)(e >> 32) & 0xCCCCCCCCu, (uint32_t)(v >> 32) & 0xCCCCCCCCu);
-            const uint4 a0 = *reinterpret_cast<const uint4 *>(abase0 + s * ustride_a);
-            const uint4 a1 = *reinterpret_cast<const uint4 *>(abase0 + s * ustride_a + 16);
-            const uint32_t sa0 = sbase0[s * ustride_s];
-            const float4_t d0 = mfma_f8f4(a0, a1, bw, sa0);
-            const float sc = S8 ? (float)(int32_t)sbits[i] : f16_bits_to_float((uint16_t)sbits[i]);
-            if constexpr (TERMS_PER_MFMA == 2) {
-#pragma unroll
-                for (int m = 0; m < M; ++m) acc[m] = fmaf(sc, d0[m] + d0[2 + m], acc[m]);
-            } else {
-                const uint4 b0 = *reinterpret_cast<const uint4 *>(abase1 + s * ustride_a);
-                const uint4 b1 = *reinterpret_cast<const uint4 *>(abase1 + s * ustride_a + 16);
-                const uint32_t sa1 = sbase1[s * ustride_s];
-                const float4_t d1 = mfma_f8f4(b0, b1, bw, sa1);
-#pragma unroll
-                for (int m = 0; m < M; ++m) acc[m] = fmaf(sc, d0[m] + d1[m], acc[m]);
-            }
-            if (i == UPW - 1 || u + 1 >= U || s == steps - 1) {
-                // every lane stores (the other lanes into a private spare
-                // slot): a store only the holder lanes made would let the
-                // compiler sink the MFMA into that divergent branch, and a
-                // matrix instruction run under a partial EXEC mask does not
-                // see the operands of the masked lanes
-                float4_t rr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < M; ++m) rr[m] = acc[m];
-                red[holder ? (wave * kmax + (ql - qfirst)) * 16 + col : F_WAVES * kmax * 16 + lane] = rr;
-#pragma unroll
-                for (int m = 0; m < M; ++m) acc[m] = 0.f;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) asm volatile("" ::"v"(code[i].x), "v"(sbits[i]));
-    __syncthreads();
-
-    // ---- 4. outputs: the 4 blocks and the wave partials of each row, in order ----
-    const int nrows = 4 * (qb - qa);
-    for (int o = tid; o < nrows * M; o += F_THREADS) {
-        const int m = o / nrows;
-        const int rl = o % nrows;
-        const int qo = rl >> 2;
-        const int n = 4 * qa + rl;
+    for (int o = tid; o < 4 * Q * M; o += blockDim.x) {
+        const int m = o / (4 * Q);
+        const int rr = o - m * 4 * Q;
+        const int n = n0 + rr;
         if (n >= N) continue;
-        const int w0 = (qo * steps) / UPW;
-        const int w1 = (qo * steps + steps - 1) / UPW;
+        const int q = rr >> 2, rw = rr & 3;
         float y = 0.f;
-        for (int w = w0; w <= w1; ++w) {
-            const int qf = min(w * UPW, U - 1) / steps;
-            const float4_t *pp = red + (w * kmax + (qo - qf)) * 16 + 4 * (rl & 3);
-            y += (pp[0][m] + pp[1][m]) + (pp[2][m] + pp[3][m]);
+        for (int w = 0; w < nw; ++w) {
+            const float *pp = red + ((w * Q + q) * 16 + 4 * rw) * M + m;
+            y += (pp[0] + pp[M]) + (pp[2 * M] + pp[3 * M]);
         }
         y *= 0.5f;   // the weights were +-2
-        if constexpr (S8) y *= R[n];
+        if constexpr (S8) y *= Rf[n];
         if (y_dtype == 2) store_out<2>(Y, (int64_t)m * N + n, y);
         else if (y_dtype == 1) store_out<1>(Y, (int64_t)m * N + n, y);
         else store_out<0>(Y, (int64_t)m * N + n, y);
@@ -388,38 +365,56 @@ __global__ __launch_bounds__(F_THREADS) void gemv_fp4_kernel(const uint16_t *__r
 }
 
 struct F4Shape {
-    int steps, grid, upw, opt, kmax;
+    int steps, spw, nw, q, grid;
     size_t lds;
 };
 
+// Instantiated (steps per wave, quads) pairs, minus the two that spill
+// registers at this M.
+bool f4_instantiated(int64_t M, int spw, int q) {
+    bool in = false;
+#define TERN_F4_CASE(SP, QQ) in = in || (spw == SP && q == QQ);
+    TERN_F4_TABLE(TERN_F4_CASE)
+#undef TERN_F4_CASE
+    return in && !(M == 1 && spw == 1 && q == 17) && !(M == 4 && spw == 2 && q == 8);
+}
+
+size_t f4_lds(int64_t M, int nw, int q) {
+    return (size_t)nw * 8 * M * (F_IMG + 4) + (size_t)nw * q * 16 * M * 4 + (size_t)64 * M * 4 + 16;
+}
+
 F4Shape f4_shape(int64_t M, int64_t N, int64_t K) {
     F4Shape g{};
-    const int64_t groups = K / 128;
-    g.steps = (int)((groups + F_BPU - 1) / F_BPU);
-    const int64_t nquads = (N + 3) / 4;
-    int64_t grid = 256;
-    while ((nquads + grid - 1) / grid * g.steps > (int64_t)F_WAVES * F_MAX_UPW && grid < nquads) grid += 256;
-    g.grid = (int)std::min<int64_t>(grid, nquads);
-    const int64_t qmax = (nquads + g.grid - 1) / g.grid;
-    const int64_t units = qmax * g.steps;
-    int upw = (int)((units + F_WAVES - 1) / F_WAVES);
-    if (upw > F_MAX_UPW) upw = 0;
-    else if (upw == 5) upw = 6;
-    else if (upw == 7) upw = 8;
-    else if (upw > 8) upw = 12;
-    g.upw = upw;
-    const int64_t octs = M * g.steps * F_BPU * 16;
-    const int64_t opt = (octs + F_THREADS - 1) / F_THREADS;
-    g.opt = opt <= 1 ? 1 : opt <= 2 ? 2 : opt <= 4 ? 4 : opt <= 6 ? 6 : opt <= 9 ? 9 : 0;
-    g.kmax = upw == 0 ? 0 : (int)std::min<int64_t>(upw, (upw + g.steps - 1) / g.steps + 1);
-    const int64_t g4 = (int64_t)g.steps * F_BPU;
-    g.lds = (size_t)(M * 2 * g4 * 128 + M * 2 * g4 * 4) + (size_t)F_WAVES * g.kmax * 256 + 64 * 16 + 32;
+    g.steps = (int)((K + F_STEP - 1) / F_STEP);
+    g.spw = (g.steps + F_MAX_WAVES - 1) / F_MAX_WAVES;
+    g.nw = (g.steps + g.spw - 1) / g.spw;
+    // Quads per workgroup.  The busiest CU runs ceil(grid / CUs) workgroups
+    // of Q quads each, plus about one quad's worth of per-workgroup work
+    // (staging, reduction): pick the Q with the least of that, the larger Q
+    // on ties.  Measured at M = 1 (rows 5120 / 17408): the best Q of a sweep
+    // over 2..16 was also the model's choice, 5 / 6 (4.16 / 7.35 us); at
+    // 17408 -> 5120, 5 (7.04 us against 9.7 for 2).
+    constexpr int64_t kCUs = 256;
+    const int64_t quads = (N + 3) / 4;
+    int64_t best = -1;
+    for (int q = 1; q <= 17; ++q) {
+        if (!f4_instantiated(M, g.spw, q) || f4_lds(M, g.nw, q) > 160 * 1024) continue;
+        const int64_t grid = (quads + q - 1) / q;
+        const int64_t cost = (grid + kCUs - 1) / kCUs * (q + 1);
+        if (best < 0 || cost <= best) {
+            best = cost;
+            g.q = q;
+        }
+    }
+    if (best < 0) return g;   // q = 0: nothing fits
+    g.grid = (int)((quads + g.q - 1) / g.q);
+    g.lds = f4_lds(M, g.nw, g.q);
     return g;
 }
 
-template <int M, bool S8, int UPW, int OPT>
+template <int M, bool S8, int Q, int SPW>
 hipError_t launch_f4t(const GemmArgs &a, const F4Shape &g) {
-    auto kern = gemv_fp4_kernel<M, S8, UPW, OPT>;
+    auto kern = gemv_fp4_kernel<M, S8, Q, SPW>;
     if (g.lds > 64 * 1024) {
         // raise the dynamic-LDS limit once per device and instantiation (a
         // per-process attribute cache; not a stream operation)
@@ -435,39 +430,23 @@ hipError_t launch_f4t(const GemmArgs &a, const F4Shape &g) {
             done_mask.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(F_THREADS), g.lds, a.stream,
-                       static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y, a.y_dtype, (int)a.N, (int)a.K,
-                       (int)((a.N + 3) / 4), g.kmax);
+    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(64 * g.nw), g.lds, a.stream,
+                       static_cast<const uint16_t *>(a.X), a.W, a.S, a.Q, a.R, a.Y, a.y_dtype, (int)a.N, (int)a.K);
     return hipGetLastError();
 }
 
-template <int M, bool S8, int UPW>
-hipError_t launch_f4o(const GemmArgs &a, const F4Shape &g) {
-    switch (g.opt) {
-    case 1: return launch_f4t<M, S8, UPW, 1>(a, g);
-    case 2: return launch_f4t<M, S8, UPW, 2>(a, g);
-    case 4: return launch_f4t<M, S8, UPW, 4>(a, g);
-    case 6: return launch_f4t<M, S8, UPW, 6>(a, g);
-    default: return launch_f4t<M, S8, UPW, 9>(a, g);
-    }
-}
-
 template <int M, bool S8>
-hipError_t launch_f4u(const GemmArgs &a, const F4Shape &g) {
-    switch (g.upw) {
-    case 1: return launch_f4o<M, S8, 1>(a, g);
-    case 2: return launch_f4o<M, S8, 2>(a, g);
-    case 3: return launch_f4o<M, S8, 3>(a, g);
-    case 4: return launch_f4o<M, S8, 4>(a, g);
-    case 6: return launch_f4o<M, S8, 6>(a, g);
-    case 8: return launch_f4o<M, S8, 8>(a, g);
-    default: return launch_f4o<M, S8, 12>(a, g);
-    }
+hipError_t launch_f4s(const GemmArgs &a, const F4Shape &g) {
+#define TERN_F4_CASE(SP, QQ) \
+    if (g.spw == SP && g.q == QQ) return launch_f4t<M, S8, QQ, SP>(a, g);
+    TERN_F4_TABLE(TERN_F4_CASE)
+#undef TERN_F4_CASE
+    return hipErrorInvalidValue;
 }
 
 template <int M>
 hipError_t launch_f4m(const GemmArgs &a, const F4Shape &g) {
-    return a.Q != nullptr ? launch_f4u<M, true>(a, g) : launch_f4u<M, false>(a, g);
+    return a.Q != nullptr ? launch_f4s<M, true>(a, g) : launch_f4s<M, false>(a, g);
 }
 
 }  // namespace
@@ -475,7 +454,7 @@ hipError_t launch_f4m(const GemmArgs &a, const F4Shape &g) {
 bool gemv_fp4_fits(int64_t M, int64_t N, int64_t K, int x_dtype) {
     if (x_dtype != 1 || M < 1 || M > 4 || N < 1 || K < 128) return false;
     const F4Shape g = f4_shape(M, N, K);
-    return g.upw > 0 && g.opt > 0 && g.lds <= 160 * 1024;
+    return g.spw <= F_MAX_SPW && g.q > 0;
 }
 
 hipError_t launch_gemv_fp4(const GemmArgs &a) {

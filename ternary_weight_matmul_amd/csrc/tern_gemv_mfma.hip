@@ -248,17 +248,17 @@ __global__ __launch_bounds__(QTHREADS) void gemv_mfma_kernel(const uint16_t *__r
             const char *src = abase + s * QSTEP_BYTES;
 #pragma unroll
             for (int c = 0; c < QCHUNKS; ++c) a[c] = *reinterpret_cast<const uint4 *>(src + c * 256);
-            const uint64_t v01 = sign_nz_fields64((uint64_t)code[i].x | ((uint64_t)code[i].y << 32));
-            const uint64_t v23 = sign_nz_fields64((uint64_t)code[i].z | ((uint64_t)code[i].w << 32));
+            const uint64_t v01 = sign_nz_fields64<true>((uint64_t)code[i].x | ((uint64_t)code[i].y << 32));
+            const uint64_t v23 = sign_nz_fields64<true>((uint64_t)code[i].z | ((uint64_t)code[i].w << 32));
             float4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
             // pairs 2t', 2t'+1 of code word w against activation words 2t', 2t'+1 of block w
             auto quarter = [&](auto tc) {
                 constexpr int T = decltype(tc)::value;   // t' = 0..3
                 uint32_t p0a, p1a, p2a, p3a, p0b, p1b, p2b, p3b;
-                weight_pairs2<2 * T>(v01, p0a, p1a);
-                weight_pairs2<2 * T + 1>(v01, p0b, p1b);
-                weight_pairs2<2 * T>(v23, p2a, p3a);
-                weight_pairs2<2 * T + 1>(v23, p2b, p3b);
+                weight_pairs2<2 * T, true>(v01, p0a, p1a);
+                weight_pairs2<2 * T + 1, true>(v01, p0b, p1b);
+                weight_pairs2<2 * T, true>(v23, p2a, p3a);
+                weight_pairs2<2 * T + 1, true>(v23, p2b, p3b);
                 constexpr int cc = T >> 1;            // chunk within the block
                 constexpr int e = (T & 1) * 2;        // first word within the chunk
                 d0 = mfma4x4<XBF16>((&a[0 + cc].x)[e], (&a[0 + cc].x)[e + 1], p0a, p0b, d0);

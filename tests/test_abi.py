@@ -64,7 +64,7 @@ def mm(X=P, xd=F16, W=P, S=P, Y=P, yd=F32, M=1, N=16, K=128, G=128, path=0):
     (dict(M=5, path=1), UNSUP), (dict(path=5), UNSUP),
     (dict(M=1, K=128 * 1024, path=1), UNSUP),
     # the fp4 matrix-core decode kernel: bf16 activations only, M <= 4
-    (dict(path=4), UNSUP), (dict(xd=BF16, M=5, path=4), UNSUP), (dict(xd=BF16, M=4, K=20480, path=4), UNSUP),
+    (dict(path=4), UNSUP), (dict(xd=BF16, M=5, path=4), UNSUP), (dict(xd=BF16, M=1, K=33280, path=4), UNSUP),
     # the matrix-core decode kernel: M <= 4, activations staged whole in LDS
     (dict(M=5, path=3), UNSUP), (dict(M=4, K=20480, path=3), UNSUP), (dict(M=1, K=128 * 1024, path=3), UNSUP),
 ])

@@ -85,6 +85,25 @@ def test_ragged_shapes(M, K, N, xd, yd):
         _full(p, path)
 
 
+# The fp4 kernel's own layout: workgroups of 1 to 17 quads (4-row groups;
+# the count follows N), 512-weight steps split over up to 16 waves, 1 to 4
+# steps per wave (K up to 32768, the images of one step staged at a time), a
+# ragged last step (K off the multiple of 512: its blocks past K meet zero
+# activations and their scales are dropped), N off the multiple of 4 and of
+# the workgroup's rows, and one or many rounds of workgroups.
+FP4_LAYOUT = [(1, 128, 1), (2, 640, 17), (3, 1152, 31), (4, 4224, 33), (1, 512, 15), (1, 8320, 70),
+              (2, 16512, 48), (1, 24704, 40), (2, 32768, 33), (1, 2048, 8193), (4, 17408, 8195),
+              (3, 12416, 8200), (4, 8192, 47), (4, 32768, 1021), (4, 5120, 17407), (1, 5120, 34813),
+              (2, 20480, 5119)]
+
+
+@pytest.mark.parametrize("M,K,N", FP4_LAYOUT)
+@pytest.mark.parametrize("yd", ["bf16", "f32", "f16"])
+def test_fp4_layout_shapes(M, K, N, yd):
+    p = workloads.make_custom(M * 7 + K + N, M, K, N, x_dtype="bf16", y_dtype=yd, reserved_rate=0.02)
+    _full(p, "gemv_fp4")
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (1, 5120, 1100), (2, 2048, 24), (3, 2048, 40), (4, 10240, 16),
                                    (1, 17408, 12), (4, 17408, 77), (2, 640, 4500), (1, 1024, 40001)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
@@ -202,13 +221,15 @@ def test_agrees_with_the_valu_decode_kernel():
         assert all(_full(p, path) <= 1 for path in ["gemv"] + PATHS)
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_refuses_activations_beyond_lds(path):
-    """M = 4 with K = 20480 stages 160 KB of activations, more than the
-    workgroup's LDS: the forced path is refused before anything runs."""
-    p = workloads.make_custom(3, 4, 20480, 8, x_dtype="bf16", y_dtype="f32")
+@pytest.mark.parametrize("path,M,K", [("gemv_mfma", 4, 20480), ("gemv_fp4", 1, 33280)])
+def test_refuses_shapes_beyond_its_layout(path, M, K):
+    """The 4x4x4 kernel stages all activations of a workgroup (M = 4, K =
+    20480: 160 KB, more than its LDS); the fp4 kernel takes at most 4 steps
+    of 512 weights per wave over 16 waves (K <= 32768).  Beyond that the
+    forced path is refused before anything runs."""
+    p = workloads.make_custom(3, M, K, 8, x_dtype="bf16", y_dtype="f32")
     x, w, s = problem_to_device(p)
-    y = torch.full((4, 8), 5.0, dtype=torch.float32, device=device())
+    y = torch.full((M, 8), 5.0, dtype=torch.float32, device=device())
     with pytest.raises(tern.TernError) as err:
         tern.matmul_into(x, w, s, y, path=path)
     assert err.value.status == 6
