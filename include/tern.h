@@ -201,6 +201,19 @@ tern_status tern_matmul_s8(const void *X, tern_dtype x_dtype, const uint8_t *pac
                            const float *row_factor, void *Y, tern_dtype y_dtype, int64_t M, int64_t N,
                            int64_t K, int32_t group, tern_path path, hipStream_t stream);
 
+/*
+ * tern_stream_copy -- calibration, not part of the method: stream `bytes`
+ * bytes of src with 16-byte loads (one instruction reads 1 KB of
+ * consecutive bytes, every load of a thread issued before any is used) and,
+ * when dst is not NULL, write them to dst.  With dst NULL it only reads.
+ * It gives the plain-read (and copy) ceiling the decode kernels are timed
+ * against, and a kernel of known traffic for scaling the HBM byte counters.
+ * bytes % 16 == 0 and bytes <= 2^40 (TERN_ERR_SHAPE); src and dst 16-byte
+ * aligned (TERN_ERR_ALIGN); src NULL with bytes > 0 is TERN_ERR_NULL;
+ * bytes == 0 launches nothing.  Asynchronous on `stream`.
+ */
+tern_status tern_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ from ._lib import (  # noqa: F401
     library_path,
 )
 from .ops import (block_map, dequant, matmul, matmul_blockmap, matmul_blockmap_into, matmul_into,  # noqa: F401
-                  matmul_s8, matmul_s8_into, pack, quantize_scales, shard_columns, shard_k, unpack)
+                  matmul_s8, matmul_s8_into, pack, quantize_scales, shard_columns, shard_k, stream_copy, unpack)
 
 GROUP = 128
 GEMV_MAX_M = 4

@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
     L.tern_quantize_scales.restype = c_int
     L.tern_matmul_s8.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, i64, i64, i64, i32, c_int, vp]
     L.tern_matmul_s8.restype = c_int
+    L.tern_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
+    L.tern_stream_copy.restype = c_int
     return L
 
 

@@ -59,10 +59,10 @@
 //     lanes x 32 bytes per step, then their block-scale bytes): no
 //     workgroup barrier before the products, and one step's A registers
 //     serve all Q quads.
-//   * At the end the used lanes write their sums to LDS and after one
-//     barrier each output adds its 4 blocks and the waves in a fixed order
-//     (deterministic), halves the sum (the weights are +-2) and rounds it to
-//     the output type.
+//   * At the end the used lanes write their sums to LDS, the 4 blocks of a
+//     row side by side; after one barrier each output adds its blocks and the
+//     waves in a fixed order (deterministic), halves the sum (the weights are
+//     +-2) and rounds it to the output type.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -201,9 +201,9 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const int n0 = blockIdx.x * 4 * Q;
     const int rows = min(4 * Q, N - n0);
     char *wimg = ldsb + wave * SL;   // one step's images, reused step after step
-    float *red = reinterpret_cast<float *>(ldsb + nw * SL);   // [nw][Q][16][M], then [64][M] spares
+    float *red = reinterpret_cast<float *>(ldsb + nw * SL);   // [M][nw][4 Q rows][4 blocks], then 64 spares
     float *spare = red + nw * Q * 16 * M;
-    char *spare_byte = reinterpret_cast<char *>(spare + 64 * M);
+    char *spare_byte = reinterpret_cast<char *>(spare + 64);
 
     // ---- 1. loads: this lane's activation octets first, then every code and
     //         scale load of the wave (rows past N read zeros; bytes past K
@@ -334,27 +334,32 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
 #pragma unroll
         for (int q = 0; q < Q; ++q) asm volatile("" ::"v"(code[st][q].x), "v"(sbits[st][q]));
 
-    // ---- 4. the lanes with p = c hold the used sums: they write them (the
-    //         others into spares, so every lane stores and no MFMA sits under
-    //         a partial EXEC mask), then each output adds its 4 blocks and the
-    //         waves in order ----
-    const bool holder = p == c;
+    // ---- 4. the used sums sit in the lanes with p = c (block c of row r,
+    //         column 4 r + c): each writes its sum to LDS at [m][wave][row][c]
+    //         (the other lanes into a spare word, so every lane stores and no
+    //         MFMA sits under a partial EXEC mask); after the barrier each
+    //         output reads its 4 blocks as one 16-byte word per wave (adjacent
+    //         outputs, adjacent words) and adds the waves in order ----
+    // (the index is chosen with a mask the compiler cannot see through, so
+    // the store stays one branch-free instruction)
+    const int hmask = (int)opaque_lanes(p == c);
+    const int spare_at = nw * Q * 16 * M + lane;
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            *(holder ? red + ((wave * Q + q) * 16 + col) * M + m : spare + lane * M + m) = acc[q][m];
+            red[spare_at + (((((m * nw + wave) * Q + q) * 4 + r) * 4 + c - spare_at) & hmask)] = acc[q][m];
     __syncthreads();
     for (int o = tid; o < 4 * Q * M; o += blockDim.x) {
         const int m = o / (4 * Q);
         const int rr = o - m * 4 * Q;
         const int n = n0 + rr;
         if (n >= N) continue;
-        const int q = rr >> 2, rw = rr & 3;
+        const float4_t *pp = reinterpret_cast<const float4_t *>(red) + m * nw * 4 * Q + rr;
         float y = 0.f;
         for (int w = 0; w < nw; ++w) {
-            const float *pp = red + ((w * Q + q) * 16 + 4 * rw) * M + m;
-            y += (pp[0] + pp[M]) + (pp[2 * M] + pp[3 * M]);
+            const float4_t v = pp[w * 4 * Q];
+            y += (v[0] + v[1]) + (v[2] + v[3]);
         }
         y *= 0.5f;   // the weights were +-2
         if constexpr (S8) y *= Rf[n];
@@ -380,7 +385,7 @@ bool f4_instantiated(int64_t M, int spw, int q) {
 }
 
 size_t f4_lds(int64_t M, int nw, int q) {
-    return (size_t)nw * 8 * M * (F_IMG + 4) + (size_t)nw * q * 16 * M * 4 + (size_t)64 * M * 4 + 16;
+    return (size_t)nw * 8 * M * (F_IMG + 4) + (size_t)nw * q * 16 * M * 4 + 64 * 4 + 16;
 }
 
 F4Shape f4_shape(int64_t M, int64_t N, int64_t K) {

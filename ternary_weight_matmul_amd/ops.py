@@ -235,3 +235,20 @@ def shard_k(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, rank: i
     k0, k1 = g0 * group, g1 * group
     return (x[:, k0:k1].contiguous(), packed[:, k0 // 4:k1 // 4].contiguous(),
             scales[:, g0:g1].contiguous())
+
+
+def stream_copy(src: torch.Tensor, dst: Optional[torch.Tensor] = None, nbytes: Optional[int] = None) -> None:
+    """Calibration only: stream ``nbytes`` bytes of ``src`` (all of it by default) and copy
+    them into ``dst`` when given; with no ``dst`` the bytes are only read.  Device tensors,
+    contiguous, 16-byte aligned; nbytes a multiple of 16."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds src")
+    dptr = 0
+    if dst is not None:
+        if not dst.is_cuda or not dst.is_contiguous() or dst.numel() * dst.element_size() < n:
+            raise ValueError("dst must be a contiguous device tensor of at least nbytes")
+        dptr = dst.data_ptr()
+    _check(lib.tern_stream_copy(src.data_ptr(), dptr, n, _stream(src)), "tern_stream_copy")

@@ -169,3 +169,15 @@ def mmb(X=P, xd=BF16, W=P, S=P, MAP=P, Y=P, yd=F32, M=1, N=16, K=128, G=128):
 def test_matmul_blockmap_rejects(kw, want):
     assert mmb(**kw) == want
     assert mmb(X=0, W=0, S=0, MAP=0, Y=0, M=0) == OK
+
+
+def test_stream_copy_rejects():
+    """The calibration read/copy validates before launching; zero bytes launch nothing."""
+    f = L.tern_stream_copy
+    assert f(0, 0, 0, None) == OK
+    assert f(P, P, 0, None) == OK
+    assert f(0, 0, 16, None) == NULL
+    assert f(P, 0, 17, None) == SHAPE
+    assert f(P, 0, (1 << 40) + 16, None) == SHAPE
+    assert f(P + 8, 0, 16, None) == ALIGN
+    assert f(P, P + 4, 16, None) == ALIGN
