@@ -14,8 +14,11 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer the caller allocated and owns.  The
- *     library allocates nothing, keeps no state between calls and never
- *     frees or retains a caller buffer.
+ *     library allocates no device memory, uses no scratch buffer and never
+ *     frees or retains a caller buffer.  Its only state across calls is a
+ *     per-process record, per device and kernel instantiation, that the
+ *     kernel's dynamic-LDS limit has been raised (hipFuncSetAttribute, done
+ *     once on first use); no call's result depends on an earlier call.
  *   - Every tensor is dense, row-major and contiguous.  Pointers to X, W, T
  *     and packed bytes must be 16-byte aligned (TERN_ERR_ALIGN otherwise);
  *     scales need 2-byte and Y its element alignment.

@@ -25,9 +25,12 @@
 //   * small workgroups (8 rows, or 12 when K > 16384) spread a layer's rows
 //     over many CUs, so no CU runs much more than its share.
 // A short-step variant (gemv_short_kernel, below) serves M <= 4 when N is at
-// most 5120 and K at most 5120 (M = 1) or 8192: one workgroup per CU at
-// most, 512-weight steps and 8 code bytes per lane and row; each decoded
-// pair feeds every activation row.
+// most 5120 and K at most 5120 (M = 1) or 8192, and M = 2 with K <= 8192 on
+// layers of 12288 rows or more: 512-weight steps and 8 code bytes per lane
+// and row, each decoded pair feeding every activation row; workgroups of
+// 4 ceil(N / 1024) <= 20 rows (at most 256 of them, one per CU) up to N =
+// 5120, and of 20 rows over several rounds of workgroups on the wide M = 2
+// layers.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -250,11 +253,14 @@ hipError_t launch_gemv_m(const GemmArgs &a) {
 }
 
 
-// ---- short-step variant: M <= 4, N <= 5120, K <= 5120 (M = 1) or 8192 ----
-// The layer's rows fit in one workgroup per CU: a workgroup covers 4 JR rows
-// with JR = ceil(N / 1024) <= 5, so there are at most 256 workgroups and each
-// CU gets the same share (8-row workgroups would leave half of the CUs with
-// one workgroup more than the others).  Each wave takes one 512-weight step,
+// ---- short-step variant: M <= 4, N <= 5120, K <= 5120 (M = 1) or 8192;
+//      also M = 2, K <= 8192, N >= 12288 ----
+// Up to N = 5120 the layer's rows fit in one workgroup per CU: a workgroup
+// covers 4 JR rows with JR = ceil(N / 1024) <= 5, so there are at most 256
+// workgroups and each CU gets the same share (8-row workgroups would leave
+// half of the CUs with one workgroup more than the others).  On the wide
+// M = 2 layers the workgroups keep 20 rows (JR = 5) and run in several
+// rounds, N / 20 of them.  Each wave takes one 512-weight step,
 // so a workgroup has ceil(K / 512) <= 16 waves, and lane (r, kk) reads the
 // 8 code bytes (32 weights) of chunk kk of rows n0 + 4j + r.  The step's
 // activations (32 blocks of 16) are staged pair-interleaved in the wave's

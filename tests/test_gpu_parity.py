@@ -276,6 +276,38 @@ def test_large_tiles_exact_bit_exact(M, K, N):
     assert np.array_equal(got, O().round(Y, "f32"))
 
 
+# The cost model sends M=320, 1024 -> 17408 to the 192 x 256 tiles (136 of
+# them; 2 x 68 against 136 tiles of 256 x 256 and 816 of 128 x 64) and M=256,
+# 1024 -> 17408 to the plain 128 x 64 tiles with one K group (544 tiles: more
+# than the CUs, so no K split; 272 tiles of 128 x 128).  K = 1024 is 16 steps
+# of 64, so the steady-state loop that alternates the two register sets of
+# staged loads runs many times in both.
+FULL_K_TILES = [(320, 1024, 17408), (256, 1024, 17408)]
+
+
+@pytest.mark.parametrize("M,K,N", FULL_K_TILES)
+def test_large_tiles_full_k(M, K, N):
+    """Every output of the 192 x 256 and the one-group 128 x 64 tile kernels at
+    16 K steps, against the oracle (bf16 output: the rounding epilogue too)."""
+    p = workloads.make_custom(M + N + K, M, K, N, x_dtype="f16", y_dtype="bf16", reserved_rate=0.02)
+    _full(p, "auto")
+
+
+@pytest.mark.parametrize("M,K,N", FULL_K_TILES)
+def test_large_tiles_full_k_exact_bit_exact(M, K, N):
+    """Exact arithmetic (integer activations in [-8, 8], power-of-two scales)
+    on the same two tile kernels: bit-identical to the oracle."""
+    rng = np.random.default_rng(99 + M)
+    xbits = rng.integers(-8, 9, (M, K)).astype(np.float16).view(np.uint16)
+    P = O().pack(workloads.draw_ternary(78, N, K))
+    sbits = (2.0 ** rng.integers(-4, 1, (N, K // 128))).astype(np.float16).view(np.uint16)
+    Y, _ = O().matmul(xbits, "f16", P, sbits, M, N, K, threads=8)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=device())
+    tern.matmul_into(bits_to_device(xbits, "f16"), torch.from_numpy(P).to(device()), bits_to_device(sbits, "f16"), y)
+    got = O().decode(out_bits(y, "f32"), "f32")
+    assert np.array_equal(got, O().round(Y, "f32"))
+
+
 # ---------------------------------------------------------------------------
 # invariants of the method, exact on the GPU
 # ---------------------------------------------------------------------------
