@@ -104,6 +104,21 @@ def test_fp4_layout_shapes(M, K, N, yd):
     _full(p, "gemv_fp4")
 
 
+# More ragged fp4 shapes at M <= 2: K off the multiple of 512 and 1024 (the
+# blocks of the last step past K meet zero activations, their scales are
+# dropped), N odd and off the workgroup's rows, 1 to 4 steps per wave (K up
+# to 32768).
+FP4_MORE_RAGGED = [(1, 128, 1), (1, 640, 3), (2, 896, 5), (1, 1152, 21), (2, 5120, 5119), (1, 5120, 17409), (2, 17408, 77),
+         (1, 16512, 33), (2, 24704, 41), (1, 32768, 10), (2, 1024, 4097), (1, 3200, 257)]
+
+
+@pytest.mark.parametrize("M,K,N", FP4_MORE_RAGGED)
+@pytest.mark.parametrize("yd", ["bf16", "f32"])
+def test_fp4_more_ragged_shapes(M, K, N, yd):
+    p = workloads.make_custom(M * 11 + K + N, M, K, N, x_dtype="bf16", y_dtype=yd, reserved_rate=0.02)
+    _full(p, "gemv_fp4")
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 64), (1, 5120, 1100), (2, 2048, 24), (3, 2048, 40), (4, 10240, 16),
                                    (1, 17408, 12), (4, 17408, 77), (2, 640, 4500), (1, 1024, 40001)])
 @pytest.mark.parametrize("xd", ["f16", "bf16"])
