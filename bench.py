@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--replays", type=int, default=5, help="timed replays of the graph (median reported)")
     ap.add_argument("--config", type=int, default=2, help="workload id (workloads.CONFIGS)")
     ap.add_argument("--shape", type=int, default=0, help="shape index inside the workload")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "gemv_mfma", "gemv_fp4"])
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma", "gemv_mfma", "gemv_fp4", "gemv_b16"])
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

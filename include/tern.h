@@ -62,16 +62,20 @@ typedef enum {
     TERN_PATH_AUTO = 0, /* choose by shape (what tern_matmul does): for M <= 4, GEMV_FP4 with
                            bf16 X (K <= 32768), else with fp16 X GEMV_MFMA for M = 3, 4 where
                            it fits and GEMV for M <= 2 or where GEMV_MFMA does not fit;
+                           GEMV_B16 for 5 <= M <= 16 with N >= 16384 and K <= 8192;
                            MFMA for every other shape */
     TERN_PATH_GEMV = 1, /* VALU sign-select decode kernel; M <= TERN_GEMV_MAX_M */
     TERN_PATH_MFMA = 2, /* LDS-staged activations + in-register weight decode + MFMA; any M */
     TERN_PATH_GEMV_MFMA = 3, /* decode kernel whose sign-select sums run on the matrix cores
                                 (v_mfma_f32_4x4x4_16b on +-2 / 0 operands); M <= 4, with
                                 the activations X[M,K] staged whole in LDS */
-    TERN_PATH_GEMV_FP4 = 4  /* decode kernel with the weights as 4-bit (e2m1 +-2 / 0) matrix-core
+    TERN_PATH_GEMV_FP4 = 4, /* decode kernel with the weights as 4-bit (e2m1 +-2 / 0) matrix-core
                                operands and each bf16 activation split exactly into two e4m3
                                terms with a power-of-two scale per 32 (v_mfma_scale_f32_
                                16x16x128_f8f6f4); bf16 X only, M <= 4, K <= 32768 */
+    TERN_PATH_GEMV_B16 = 5  /* decode kernel for batches of up to 16 rows: +-2 / 0 weight
+                               operands of v_mfma_f32_16x16x32 against activation fragments
+                               held in registers, waves splitting K; M <= 16, K <= 2^20 */
 } tern_path;
 
 #define TERN_GROUP 128
@@ -126,7 +130,8 @@ tern_status tern_matmul(const void *X, tern_dtype x_dtype, const uint8_t *packed
  * kernel family (for tests that compare the two, and for benchmarks).
  * TERN_PATH_GEMV, TERN_PATH_GEMV_MFMA or TERN_PATH_GEMV_FP4 with M >
  * TERN_GEMV_MAX_M, or with an activation block too large for on-chip staging,
- * and TERN_PATH_GEMV_FP4 with fp16 activations, return TERN_ERR_UNSUPPORTED.
+ * TERN_PATH_GEMV_FP4 with fp16 activations, and TERN_PATH_GEMV_B16 with M > 16
+ * or K > 2^20, return TERN_ERR_UNSUPPORTED.
  */
 tern_status tern_matmul_path(const void *X, tern_dtype x_dtype, const uint8_t *packed_W,
                              const uint16_t *scales, void *Y, tern_dtype y_dtype, int64_t M,

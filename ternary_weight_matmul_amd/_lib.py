@@ -18,7 +18,7 @@ STATUS = {
     7: "TERN_ERR_HIP",
 }
 DTYPE_CODE = {"f16": 0, "bf16": 1, "f32": 2}
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_GEMV_MFMA, PATH_GEMV_FP4 = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_GEMV_MFMA, PATH_GEMV_FP4, PATH_GEMV_B16 = 0, 1, 2, 3, 4, 5
 
 
 class TernError(RuntimeError):

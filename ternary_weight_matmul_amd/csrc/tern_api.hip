@@ -98,9 +98,21 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K) {
 // 17408 -> 5120 12.7 against 23.9 and 15.9).  With fp16 activations the
 // 4x4x4 matrix-core kernel takes M = 3, 4 (M = 4: 5120 -> 17408 11.3 us
 // against 13.4, 5120 -> 5120 6.1 against the VALU kernel's 6.5).
+//
+// For 5 <= M <= 16 the 16-row decode kernel beats the MFMA tiles where
+// there are many weight rows and K is not long (graph-timed, bf16, weights
+// rotated over 2 GB; M = 16: 5120 -> 34816 23.0 us against 31.1, 8192 ->
+// 28672 34.0 against 40.5, 5120 -> 17408 16.9 against 19.0; M = 8 / 5 at
+// 5120 -> 17408 16.9 / 16.8 against 19.1 / 18.6).  With N <= 15360, or K =
+// 17408 (17408 -> 5120: 19.7 against 18.8), the tiles are as fast or faster.
+bool auto_b16(int64_t M, int64_t N, int64_t K) {
+    return M >= 5 && M <= 16 && N >= 16384 && K <= 8192 && tern::gemv_b16_fits(M, N, K);
+}
+
 tern_path auto_path(const tern::GemmArgs &a) {
     if (a.M <= 4 && a.x_dtype == 1 && tern::gemv_fp4_fits(a.M, a.N, a.K, 1)) return TERN_PATH_GEMV_FP4;
     if (a.M >= 3 && a.M <= 4 && a.x_dtype == 0 && tern::gemv_mfma_fits(a.M, a.N, a.K)) return TERN_PATH_GEMV_MFMA;
+    if (auto_b16(a.M, a.N, a.K)) return TERN_PATH_GEMV_B16;
     return auto_gemv(a.M, a.N, a.K) ? TERN_PATH_GEMV : TERN_PATH_MFMA;
 }
 
@@ -108,13 +120,14 @@ tern_path auto_path(const tern::GemmArgs &a) {
 // before anything is launched).
 tern_status check_path(tern_path path, tern_dtype x_dtype, int64_t M, int64_t N, int64_t K) {
     if (path != TERN_PATH_AUTO && path != TERN_PATH_GEMV && path != TERN_PATH_MFMA && path != TERN_PATH_GEMV_MFMA &&
-        path != TERN_PATH_GEMV_FP4)
+        path != TERN_PATH_GEMV_FP4 && path != TERN_PATH_GEMV_B16)
         return TERN_ERR_UNSUPPORTED;
     if (M == 0 || N == 0 || K == 0) return TERN_OK;
     if (path == TERN_PATH_GEMV && !gemv_fits(M, K)) return TERN_ERR_UNSUPPORTED;
     if (path == TERN_PATH_GEMV_MFMA && !tern::gemv_mfma_fits(M, N, K)) return TERN_ERR_UNSUPPORTED;
     if (path == TERN_PATH_GEMV_FP4 && !tern::gemv_fp4_fits(M, N, K, x_dtype == TERN_BF16 ? 1 : 0))
         return TERN_ERR_UNSUPPORTED;
+    if (path == TERN_PATH_GEMV_B16 && !tern::gemv_b16_fits(M, N, K)) return TERN_ERR_UNSUPPORTED;
     return TERN_OK;
 }
 
@@ -124,6 +137,7 @@ hipError_t dispatch(const tern::GemmArgs &a, tern_path path) {
     case TERN_PATH_MFMA: return tern::launch_gemm(a);
     case TERN_PATH_GEMV_MFMA: return tern::launch_gemv_mfma(a);
     case TERN_PATH_GEMV_FP4: return tern::launch_gemv_fp4(a);
+    case TERN_PATH_GEMV_B16: return tern::launch_gemv_b16(a);
     default: {
         const tern_path p = auto_path(a);
         return p == TERN_PATH_AUTO ? hipErrorInvalidValue : dispatch(a, p);

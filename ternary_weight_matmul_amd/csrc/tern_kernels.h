@@ -41,6 +41,11 @@ hipError_t launch_gemv_mfma(const GemmArgs &a);
 bool gemv_fp4_fits(int64_t M, int64_t N, int64_t K, int x_dtype);
 hipError_t launch_gemv_fp4(const GemmArgs &a);
 
+// Decode-path kernel for batches of 1 <= M <= 16 rows: +-2 / 0 weight operands
+// of v_mfma_f32_16x16x32 against activation fragments held in registers.
+bool gemv_b16_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_b16(const GemmArgs &a);
+
 // Decode-path GEMV that skips the blocks MAP does not mark (1 <= M <= 2).
 hipError_t launch_gemv_skip(const GemmArgs &a, const uint32_t *map);
 size_t gemv_skip_lds_bytes(int64_t M, int64_t K);

@@ -11,11 +11,13 @@ from typing import Optional
 
 import torch
 
-from ._lib import DTYPE_CODE, PATH_AUTO, PATH_GEMV, PATH_GEMV_FP4, PATH_GEMV_MFMA, PATH_MFMA, TernError, lib
+from ._lib import (DTYPE_CODE, PATH_AUTO, PATH_GEMV, PATH_GEMV_B16, PATH_GEMV_FP4, PATH_GEMV_MFMA, PATH_MFMA,
+                   TernError, lib)
 
 _TORCH_CODE = {torch.float16: DTYPE_CODE["f16"], torch.bfloat16: DTYPE_CODE["bf16"],
                torch.float32: DTYPE_CODE["f32"]}
-_PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA, "gemv_mfma": PATH_GEMV_MFMA, "gemv_fp4": PATH_GEMV_FP4}
+_PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA, "gemv_mfma": PATH_GEMV_MFMA,
+          "gemv_fp4": PATH_GEMV_FP4, "gemv_b16": PATH_GEMV_B16}
 
 
 def _stream(t: torch.Tensor) -> int:

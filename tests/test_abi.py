@@ -61,8 +61,10 @@ def mm(X=P, xd=F16, W=P, S=P, Y=P, yd=F32, M=1, N=16, K=128, G=128, path=0):
     (dict(X=0), NULL), (dict(W=0), NULL), (dict(S=0), NULL), (dict(Y=0), NULL),
     (dict(X=P + 8), ALIGN), (dict(W=P + 4), ALIGN), (dict(S=P + 1), ALIGN), (dict(Y=P + 2), ALIGN),
     (dict(Y=P + 1, yd=F16), ALIGN),
-    (dict(M=5, path=1), UNSUP), (dict(path=5), UNSUP),
+    (dict(M=5, path=1), UNSUP), (dict(path=6), UNSUP),
     (dict(M=1, K=128 * 1024, path=1), UNSUP),
+    # the 16-row decode kernel: M <= 16, K <= 2^20
+    (dict(M=17, path=5), UNSUP), (dict(M=4, K=(1 << 20) + 128, path=5), UNSUP),
     # the fp4 matrix-core decode kernel: bf16 activations only, M <= 4
     (dict(path=4), UNSUP), (dict(xd=BF16, M=5, path=4), UNSUP), (dict(xd=BF16, M=1, K=33280, path=4), UNSUP),
     # the matrix-core decode kernel: M <= 4, activations staged whole in LDS
@@ -117,7 +119,8 @@ def mm8(X=P, xd=BF16, W=P, Q=P, R=P, Y=P, yd=F32, M=1, N=16, K=128, G=128, path=
     (dict(xd=F32), DTYPE), (dict(yd=9), DTYPE),
     (dict(X=0), NULL), (dict(W=0), NULL), (dict(Q=0), NULL), (dict(R=0), NULL), (dict(Y=0), NULL),
     (dict(X=P + 8), ALIGN), (dict(W=P + 4), ALIGN), (dict(R=P + 2), ALIGN), (dict(Y=P + 2), ALIGN),
-    (dict(M=5, path=1), UNSUP), (dict(path=5), UNSUP), (dict(M=5, path=3), UNSUP), (dict(xd=F16, path=4), UNSUP),
+    (dict(M=5, path=1), UNSUP), (dict(path=6), UNSUP), (dict(M=5, path=3), UNSUP), (dict(xd=F16, path=4), UNSUP),
+    (dict(M=17, path=5), UNSUP),
 ])
 def test_matmul_s8_rejects(kw, want):
     assert mm8(**kw) == want
