@@ -10,10 +10,11 @@
 // Why a kernel of its own.  With 5 to 16 activation rows every weight meets
 // several rows, so the sign-select sums are a small dense contraction, but
 // the weights are still read once and dominate the bytes.  The 16-row tiles
-// of the batched kernel stage the activations through LDS behind a barrier
-// per iteration and re-stage them for every 32 output columns; here the
-// activation fragments go straight into registers and serve several column
-// blocks, and the only barriers are the two of the final reduction.
+// of the batched kernel stage the activations through LDS behind a
+// workgroup barrier per iteration and re-stage them for every 32 output
+// columns; here each wave stages its own activations, one group at a time,
+// and uses them for up to 64 output columns, and the only workgroup
+// barriers are the two of the final reduction.
 //
 // Layout.  A workgroup owns NB column blocks (16 NB consecutive weight rows)
 // over all of K.  Its waves split K in steps of 512 weights (128 code bytes of
