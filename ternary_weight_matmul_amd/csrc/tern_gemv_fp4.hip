@@ -190,7 +190,10 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nw = blockDim.x >> 6;
+    // waves of the workgroup, as the host sizes it (from K and SPW rather
+    // than the block size, whose hidden-argument load would sit before the
+    // address arithmetic of every wave)
+    const int nw = ((K + F_STEP - 1) / F_STEP + SPW - 1) / SPW;
     const int p = lane >> 4;        // K slice of the lane (A and B)
     const int col = lane & 15;      // B column: 4 r + c
     const int r = col >> 2;
@@ -221,6 +224,9 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const char *sbase = S8 ? reinterpret_cast<const char *>(Qs + (int64_t)n0 * groups)
                            : reinterpret_cast<const char *>(S + (int64_t)n0 * groups);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sbase, (uint32_t)(rows * groups * SB));
+    // per step, the scales go out before the codes: the wait counter counts
+    // loads in order, so quad q's MFMA then waits for code q alone, not for
+    // every code load issued before a later scale
     uint2 code[SPW][Q];
     uint32_t sbits[SPW][Q];
 #pragma unroll
@@ -229,16 +235,21 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
         const int blk = min(4 * s + c, groups - 1);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int off = (4 * q + r) * row_bytes + s * (F_STEP / 4) + c * 32 + p * 8;
-            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, 2 /* nt */));
-            code[st][q] = make_uint2(v[0], v[1]);
             const int soff = ((4 * q + r) * groups + blk) * SB;
             if constexpr (S8)
                 sbits[st][q] = (uint32_t)(int32_t)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, 0);
             else
                 sbits[st][q] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int off = (4 * q + r) * row_bytes + s * (F_STEP / 4) + c * 32 + p * 8;
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, 2 /* nt */));
+            code[st][q] = make_uint2(v[0], v[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- 2. per step: split the wave's activations and stage them as A
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
         for (int m = 0; m < M; ++m)
             red[spare_at + (((((m * nw + wave) * Q + q) * 4 + r) * 4 + c - spare_at) & hmask)] = acc[q][m];
     __syncthreads();
-    for (int o = tid; o < 4 * Q * M; o += blockDim.x) {
+    for (int o = tid; o < 4 * Q * M; o += 64 * nw) {
         const int m = o / (4 * Q);
         const int rr = o - m * 4 * Q;
         const int n = n0 + rr;
