@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--record-traffic", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR", "COPY_BYTES"),
                     help="write profiles/traffic.json for this workload from rocprofv3 --pmc csv output")
+    ap.add_argument("--profile-doc", default="", metavar="PATH",
+                    help="with --record-traffic: the profiles/ summary that gives the counters' commands")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the comparison route, the other workloads and the decode sweeps")
     ap.add_argument("--eager", action="store_true",
@@ -168,6 +170,24 @@ def _pmc_average(d: str, pattern: str):
     return {k: sum(v) / len(v) for k, v in vals.items()}, sorted(names)
 
 
+def _dominant_kernel(d: str) -> str:
+    """Base name (e.g. gemv_fp4_kernel) of the library kernel with the most dispatches in a
+    rocprofv3 --pmc output directory."""
+    import csv
+    import glob
+    import re
+
+    count = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            m = re.search(r"tern::(?:\(anonymous namespace\)::)?(\w+_kernel)", row.get("Kernel_Name", ""))
+            if m and m.group(1) != "stream_kernel":
+                count[m.group(1)] = count.get(m.group(1), 0) + 1
+    if not count:
+        raise SystemExit(f"no library kernel in {d}")
+    return max(count, key=count.get)
+
+
 def record_traffic(args):
     """Write this workload's HBM bytes per launch into profiles/traffic.json, from four
     rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the workload's
@@ -179,7 +199,7 @@ def record_traffic(args):
     cfg = workloads.CONFIGS[args.config]
     sh = cfg.shapes[args.shape]
     key = f"{cfg.name} M={sh.M} K={sh.K} N={sh.N}"
-    pat = "gemv_fp4_kernel" if args.path in ("auto", "gemv_fp4") else args.path
+    pat = _dominant_kernel(fetch_dir) if args.path == "auto" else args.path
     f, fnames = _pmc_average(fetch_dir, pat)
     w, _ = _pmc_average(write_dir, pat)
     cf, _ = _pmc_average(cfetch_dir, "stream_kernel")
@@ -200,7 +220,7 @@ def record_traffic(args):
                  "fetch_kib_per_dispatch": round(f["FETCH_SIZE"], 2), "write_kib_per_dispatch": round(w["WRITE_SIZE"], 2),
                  "copy_bytes": copy_bytes, "fetch_scale_from_copy": round(fscale, 5),
                  "write_scale_from_copy": round(wscale, 5), "hbm_bytes_per_launch": int(round(hbm)),
-                 "profile": f"profiles/{key.split()[0]}_traffic.md"}
+                 "profile": args.profile_doc or f"profiles/{key.split()[0]}_traffic.md"}
     json.dump(data, open(TRAFFIC_JSON, "w"), indent=1)
     print(json.dumps(data[key]))
 
