@@ -15,8 +15,10 @@
 //     where the code is nonzero, +0 elsewhere) -- exact for every finite
 //     scale, so the MFMA sums the pages' products directly;
 //   * LDS rows are 128 bytes with their eight 16-byte chunks XOR-swizzled by
-//     (row / 2) mod 8: the 16 lanes reading one MFMA fragment, and the lanes
-//     writing a row, touch 64 distinct banks;
+//     (row / 2) mod 8: the 16 lanes reading one MFMA fragment touch 64
+//     distinct banks, and each 8 lanes writing (16-byte writes go 8 lanes at
+//     a time) write 8 distinct chunks: 8 chunks of one X row, or one chunk of
+//     8 weight columns 2 i (+1) (in the 128 x 64 tile, 4 columns, 2-way);
 //   * both tiles are double-buffered in LDS, one barrier per step; an
 //     iteration writes step s+1 (held in registers) to LDS, issues the global
 //     loads of step s+2 (or s+3, with two register sets of staged loads) and
@@ -107,10 +109,17 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_big_kernel(const uint1
     const uint16_t *x_src3 = X + (int64_t)min(m0 + (AP > 3 ? 3 : 2) * RSTEP + xr, M - 1) * K + xc * 8;
     const int x_dst = swz(xr, xc);    // + RSTEP*ROWB j (same swizzle)
 
-    // W loader: thread t < 2 BN decodes column t/2, weights 32 h .. 32 h + 31 of the step
+    // W loader: thread t < 2 BN decodes one column's weights 32 h .. 32 h + 31 of
+    // the step.  LDS takes 16-byte writes 8 lanes (128 bytes) at a time, so
+    // with BN >= 128 each 8 consecutive threads take columns 2 i (+1), i =
+    // 0..7, of one 16-column block and one h: their chunks differ under the
+    // row swizzle, where columns 2 i and 2 i + 1 share one.  Measured at
+    // M = 2048, 5120 -> 17408: SQ_LDS_BANK_CONFLICT 15.3 M -> 0 cycles per
+    // dispatch, 355.7 -> 348.1 us; the 128 x 64 tile keeps columns t / 2
+    // (it was 2.7% slower remapped at M = 256).
     const bool w_role = (2 * BN == NT) || tid < 2 * BN;
-    const int wc_col = (tid >> 1) % BN;
-    const int wc_h = tid & 1;
+    const int wc_col = BN >= 128 ? (16 * (tid >> 5) + 2 * (tid & 7) + ((tid >> 3) & 1)) % BN : (tid >> 1) % BN;
+    const int wc_h = BN >= 128 ? (tid >> 4) & 1 : tid & 1;
     const int64_t wn_g = min(n0 + wc_col, N - 1);                           // clamped: never stored
     const uint8_t *w_src = P + wn_g * row_bytes + 8 * wc_h;
     const uint16_t *s_src = S + wn_g * groups;   // (S8: Q + wn_g * groups)
