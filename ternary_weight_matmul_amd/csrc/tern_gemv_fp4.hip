@@ -205,9 +205,10 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const int n0 = blockIdx.x * 4 * Q;
     const int rows = min(4 * Q, N - n0);
     char *wimg = ldsb + wave * SL;   // one step's images, reused step after step
-    float *red = reinterpret_cast<float *>(ldsb + nw * SL);   // [M][nw][4 Q rows][4 blocks], then 64 spares
-    float *spare = red + nw * Q * 16 * M;
-    char *spare_byte = reinterpret_cast<char *>(spare + 64);
+    // [M][nw][4 Q rows][4 blocks], then 64 + 16 Q spare words (a lane that
+    // holds no used sum stores into one of them), then spare bytes
+    float *red = reinterpret_cast<float *>(ldsb + nw * SL);
+    char *spare_byte = reinterpret_cast<char *>(red + nw * Q * 16 * M + 64 + 16 * Q);
 
     // ---- 1. loads: this lane's activation octets first, then every code and
     //         scale load of the wave (rows past N read zeros; bytes past K
@@ -263,7 +264,8 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     //         2 (u % 2) + o / 2, its odds 8 bytes further.  The run's scale is
     //         byte u of the image's scale word.  A DPP quad holds one run.
     //         Products: A lane (p, i) takes image (c', h, m) of its row i, the
-    //         32 bytes of lane p; rows m >= M read as zeros. ----
+    //         32 bytes of lane p; rows m >= M read row M - 1's image (MFMA
+    //         rows are independent, and those result rows are never used). ----
     const int sg = lane >> 4;
     const int su = (lane >> 2) & 3;
     const int so = lane & 3;
@@ -271,7 +273,6 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const int ca = col >> 2;                       // A block of the lane's row
     const int ha = ONE ? (col >> 1) & 1 : 0;
     const int ma = ONE ? (col & 1) : (col & 3);
-    const uint32_t arow = opaque_lanes(ma < M);
     const int mc = min(ma, M - 1);
     float acc[Q][M];
 #pragma unroll
@@ -324,8 +325,7 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
             const int img = (ca * 2 + (ONE ? ha : h)) * M + mc;
             const uint4 d0 = *reinterpret_cast<const uint4 *>(wimg + img * F_IMG + p * 32);
             const uint4 d1 = *reinterpret_cast<const uint4 *>(wimg + img * F_IMG + p * 32 + 16);
-            a[h] = (int8v_t){(int)(d0.x & arow), (int)(d0.y & arow), (int)(d0.z & arow), (int)(d0.w & arow),
-                             (int)(d1.x & arow), (int)(d1.y & arow), (int)(d1.z & arow), (int)(d1.w & arow)};
+            a[h] = (int8v_t){(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w, (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
             sa[h] = (unsigned char)wimg[IMGS * F_IMG + img * 4 + p];
         }
         const bool blk_ok = 4 * s + c < groups;
@@ -356,10 +356,12 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
     const int hmask = (int)opaque_lanes(p == c);
     const int spare_at = nw * Q * 16 * M + lane;
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
+    for (int m = 0; m < M; ++m) {
+        // one select per activation row; the quads then store at constant offsets
+        const int base = spare_at + ((((m * nw + wave) * Q * 4 + r) * 4 + c - spare_at) & hmask);
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-            red[spare_at + (((((m * nw + wave) * Q + q) * 4 + r) * 4 + c - spare_at) & hmask)] = acc[q][m];
+        for (int q = 0; q < Q; ++q) red[base + 16 * q] = acc[q][m];
+    }
     __syncthreads();
     // Each output's partials (one float4 of 4 block sums per wave) are summed
     // in a fixed order.  When a row of 16 lanes per output fits the
@@ -421,7 +423,7 @@ bool f4_instantiated(int64_t M, int spw, int q) {
 }
 
 size_t f4_lds(int64_t M, int nw, int q) {
-    return (size_t)nw * 8 * M * (F_IMG + 4) + (size_t)nw * q * 16 * M * 4 + 64 * 4 + 16;
+    return (size_t)nw * 8 * M * (F_IMG + 4) + (size_t)nw * q * 16 * M * 4 + (64 + 16 * (size_t)q) * 4 + 16;
 }
 
 F4Shape f4_shape(int64_t M, int64_t N, int64_t K) {
