@@ -8,36 +8,15 @@
 // block's fp16 scale at the block boundary (§1.1, §4.1 third route, §4.2);
 // activations and scales stay on chip (§4.2, §4.3).
 //
-// Weight operand.  After the field transform of tern_device.h each 2-bit
-// field is [sign, nonzero].  Read as a 4-bit e2m1 value with the field in
-// bits 3..2 of its nibble, that is -2, +2 or +-0: one AND turns the 8 odd
-// fields of a code word into 8 fp4 weights in place, and a shift by 2 plus an
-// AND the 8 even ones.  Decoding 32 weights costs 10 VALU operations (about a
-// third of a lane-op per weight, against 0.9 for 16-bit +-2 pairs), which is
-// what lets the decode keep up with HBM.
-//
-// Activation operand.  v_mfma_scale_f32_16x16x128_f8f6f4 multiplies e4m3
-// activations (A) by the e2m1 weights (B), each A row carrying a power-of-two
-// scale per 32 consecutive K.  Every bf16 activation is split exactly into two
-// e4m3 terms sharing its 32-block: hi = RNE(x / 2^e) with 2^e = 2^(E - 7) for
-// the block's largest exponent E (|x / 2^e| < 256 <= 448), and
-// lo = RNE((x - hi 2^e) / 2^(e - 4)).  The residual x - hi 2^e is a multiple
-// of the bf16 ulp of x and smaller than half the e4m3 ulp of hi, so it has at
-// most 4 significant bits: lo is exact whenever that ulp is at least the
-// smallest e4m3 subnormal, i.e. for every element within 2^13 of its block's
-// largest magnitude.  Smaller elements keep an absolute error below 2^-21 of
-// the block maximum, far inside the product's 2e-3 * sum |x s| bound.  Both
-// terms enter one MFMA as separate A rows; products of e4m3 and e2m1 values
-// are exact, sums are fp32.
-//
-// Operand layout (gfx950, measured): B lane l = column l%16, true K
-// 32 (l/16) + nibble; A lane l = row l%16, true K 16 (l/16) + byte for bytes
-// 0..15 and 64 + 16 (l/16) + byte - 16 for bytes 16..31; the A scale of lane
-// l is the one of true-K block l/16; D VGPR v of lane l is row 4 (l/16) + v,
-// column l%16.  With the fp4 decode above, true K (32p + 8d + t) holds weight
-// 32p + 16 (d/2) + 2t + (d%2) of the 128-weight block, so A slice s carries
-// the activations of weights 16s..16s+15 (bytes 0..15) and 64+16s..79+16s
-// (bytes 16..31), evens first, then odds.
+// Operands (tern_fp4.h): the weights as e2m1 +-2 / 0 (B; 10 VALU operations
+// per 32 weights, about a third of a lane-op per weight against 0.9 for
+// 16-bit +-2 pairs, which is what lets the decode keep up with HBM), each
+// bf16 activation split exactly into two e4m3 terms with a power-of-two scale
+// per 32-run (A) of v_mfma_scale_f32_16x16x128_f8f6f4.  Here both terms
+// enter one MFMA as separate A rows where M <= 2.  With the fp4 decode, A
+// slice s carries the activations of weights 16s..16s+15 (bytes 0..15) and
+// 64+16s..79+16s (bytes 16..31) of the 128-weight block, evens first, then
+// odds.
 //
 // Work layout.
 //   * B column j = 4 r + c is (row r of a 4-row quad, block c of a 512-weight
@@ -70,6 +49,7 @@
 #include <atomic>
 
 #include "tern_device.h"
+#include "tern_fp4.h"
 #include "tern_kernels.h"
 
 namespace tern {
@@ -83,9 +63,6 @@ constexpr int F_IMG = 128;           // one A image: 4 lanes x 32 bytes
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef short short2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf162v_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -98,71 +75,11 @@ __device__ __forceinline__ uint32_t opaque_lanes(bool c) {
     return m;
 }
 
-// Largest of the 8 bf16 magnitudes in q (as integers: same order as values).
-__device__ __forceinline__ uint32_t max_mag8(const uint4 &q) {
-    typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
-    auto mag = [](uint32_t v) { return __builtin_bit_cast(ushort2_t, v & 0x7FFF7FFFu); };
-    ushort2_t a = __builtin_elementwise_max(mag(q.x), mag(q.y));
-    ushort2_t b = __builtin_elementwise_max(mag(q.z), mag(q.w));
-    a = __builtin_elementwise_max(a, b);
-    return a[0] > a[1] ? a[0] : a[1];
-}
-
 // Max over the 4 lanes of a DPP quad.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
     return v;
-}
-
-// Exact two-term e4m3 split of 8 bf16 activations q (scales 2^(eh - 127),
-// 2^(el - 127)): hi and lo bytes in the A order of a half chunk, evens first
-// (even[i] = element 2i, odd[i] = element 2i + 1).
-__device__ __forceinline__ void split8(const uint4 &q, uint32_t eh, uint32_t el, uint32_t &hi_even,
-                                       uint32_t &hi_odd, uint32_t &lo_even, uint32_t &lo_odd) {
-    const float sh = __builtin_bit_cast(float, eh << 23);
-    const float sl = __builtin_bit_cast(float, el << 23);
-    const short2_t z = {0, 0};
-    // hi bytes: elements 0..3 in h01, 4..7 in h23 (one pair per 16-bit half)
-    short2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, __builtin_bit_cast(bf162v_t, q.x), sh, false);
-    h01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h01, __builtin_bit_cast(bf162v_t, q.y), sh, true);
-    short2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, __builtin_bit_cast(bf162v_t, q.z), sh, false);
-    h23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h23, __builtin_bit_cast(bf162v_t, q.w), sh, true);
-    const uint32_t hb01 = __builtin_bit_cast(uint32_t, h01), hb23 = __builtin_bit_cast(uint32_t, h23);
-    // residuals x - hi (exact in fp32), then their e4m3 bytes at the lo scale
-    auto res = [](uint32_t w, float2_t hf, int half) {
-        const float x = __builtin_bit_cast(float, half ? (w & 0xFFFF0000u) : (w << 16));
-        return x - hf[half];
-    };
-    const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb01, sh, false);
-    const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb01, sh, true);
-    const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb23, sh, false);
-    const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb23, sh, true);
-    short2_t l01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, res(q.x, f0, 0), res(q.x, f0, 1), sl, false);
-    l01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l01, res(q.y, f1, 0), res(q.y, f1, 1), sl, true);
-    short2_t l23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, res(q.z, f2, 0), res(q.z, f2, 1), sl, false);
-    l23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l23, res(q.w, f3, 0), res(q.w, f3, 1), sl, true);
-    const uint32_t lb01 = __builtin_bit_cast(uint32_t, l01), lb23 = __builtin_bit_cast(uint32_t, l23);
-    hi_even = __builtin_amdgcn_perm(hb23, hb01, 0x06040200u);
-    hi_odd = __builtin_amdgcn_perm(hb23, hb01, 0x07050301u);
-    lo_even = __builtin_amdgcn_perm(lb23, lb01, 0x06040200u);
-    lo_odd = __builtin_amdgcn_perm(lb23, lb01, 0x07050301u);
-}
-
-// D = A * B + C on the matrix cores: A e4m3 with per-lane block scale sa
-// (E8M0), B e2m1 (scale 1).
-__device__ __forceinline__ float4_t mfma_f8f4(const int8v_t &av, const uint4 &b, const float4_t &c, uint32_t sa) {
-    const int8v_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0 /* A e4m3 */, 4 /* B e2m1 */, 0,
-                                                            (int)sa, 0, 127);
-}
-
-// 8 code bytes -> 32 e2m1 weights (+-2 / 0) in the K order of the header.
-__device__ __forceinline__ uint4 fp4_weights(uint32_t w0, uint32_t w1) {
-    const uint64_t v = sign_nz_fields64<true>((uint64_t)w0 | ((uint64_t)w1 << 32));
-    const uint64_t e = shl64<2, true>(v);
-    return make_uint4((uint32_t)e & 0xCCCCCCCCu, (uint32_t)v & 0xCCCCCCCCu, (uint32_t)(e >> 32) & 0xCCCCCCCCu,
-                      (uint32_t)(v >> 32) & 0xCCCCCCCCu);
 }
 
 // (steps per wave, quads per workgroup) pairs that are instantiated.
@@ -297,10 +214,8 @@ __global__ __launch_bounds__(64 * F_MAX_WAVES) void gemv_fp4_kernel(const uint16
             xv.y &= keep;
             xv.z &= keep;
             xv.w &= keep;
-            const uint32_t mx = quad_max(max_mag8(xv));  // largest magnitude of the 32-run
-            const uint32_t eb = mx >> 7;                 // its biased exponent
-            const uint32_t eh = eb > 8 ? eb - 7 : 1;     // hi scale 2^(E - 7), at least 2^-126
-            const uint32_t el = eh > 5 ? eh - 4 : 1;     // lo scale 2^(E - 11)
+            uint32_t eh, el;   // the 32-run's hi and lo scale exponents
+            split_exponents(quad_max(max_mag8(xv)), eh, el);
             uint32_t he, ho, le, lo;
             split8(xv, eh, el, he, ho, le, lo);
             const int ih = (sg * 2 + 0) * M + m;
