@@ -160,6 +160,13 @@ def test_int8_scales(M, K, N):
     check(out_bits(y, "f32"), "f32", Y, B, f"s8 {M}x{K}x{N} {PATH}")
 
 
+def test_longest_k():
+    """K = 2^20, the largest K the kernel takes: 2048 steps over 12 waves (171
+    each), the code and activation buffer offsets near the top of their
+    32-bit range; two column blocks, the second with 4 rows."""
+    _full(workloads.make_custom(4242, 16, 1 << 20, 20, x_dtype="bf16", y_dtype="f32"))
+
+
 @pytest.mark.parametrize("M,K", [(17, 1024), (4, (1 << 20) + 128)])
 def test_refuses_shapes_beyond_its_layout(M, K):
     """At most 16 activation rows (one MFMA tile) and K <= 2^20 (32-bit buffer
