@@ -37,7 +37,9 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor figure
 METRIC = ("packed-weight GB/s & % HBM peak (M=1 GEMV); TFLOP/s & % MFMA peak (M≥256)")
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-DISPATCH_SOURCE = "ternary_weight_matmul_amd/csrc/tern_api.hip"
+# host code that picks the kernel and its launch shape: the ABI dispatch and
+# each kernel file's shape rules, so every library source counts
+DISPATCH_SOURCES = "ternary_weight_matmul_amd/csrc"
 
 
 def parse():
@@ -136,13 +138,22 @@ def kernel_code_sha256(symbols) -> str:
 
 
 def dispatch_sha256() -> str:
-    return hashlib.sha256(open(os.path.join(ROOT, DISPATCH_SOURCE), "rb").read()).hexdigest()
+    """SHA-256 over the library's sources (names and contents, sorted): a change to
+    which kernel a shape gets, or to its launch shape, changes it."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, DISPATCH_SOURCES)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_key: str):
-    """HBM bytes per launch from profiles/traffic.json, if it still describes this build:
-    the machine code of the profiled kernel (hashed from the library's code object) and
-    the host dispatch source must be the ones the counters were taken on."""
+    """HBM bytes per launch from profiles/traffic.json, if it still describes the built
+    library: the machine code of the profiled kernel (hashed from the library's code
+    object) and the library sources that choose the kernel and its launch shape must be
+    the ones the counters were taken on."""
     try:
         entry = json.load(open(TRAFFIC_JSON))[workload_key]
     except (OSError, KeyError, ValueError):
@@ -152,7 +163,7 @@ def measured_traffic(workload_key: str):
     if kernel_code_sha256(entry["kernel_symbols"]) != entry["kernel_code_sha256"]:
         return None, "kernel machine code changed since the counters were taken"
     if dispatch_sha256() != entry["dispatch_sha256"]:
-        return None, "kernel dispatch changed since the counters were taken"
+        return None, "library sources (kernel choice or launch shape) changed since the counters were taken"
     return int(entry["hbm_bytes_per_launch"]), entry["profile"]
 
 

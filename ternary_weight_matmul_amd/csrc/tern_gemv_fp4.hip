@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 
 // (steps per wave, quads per workgroup) pairs that are instantiated.
 #define TERN_F4_TABLE(X)                                                                                       \
-    X(1, 1) X(1, 2) X(1, 3) X(1, 4) X(1, 5) X(1, 6) X(1, 8) X(1, 10) X(1, 12) X(1, 17) X(2, 1) X(2, 2) X(2, 3) \
+    X(1, 1) X(1, 2) X(1, 3) X(1, 4) X(1, 5) X(1, 6) X(1, 8) X(1, 9) X(1, 10) X(1, 12) X(1, 17) X(2, 1) X(2, 2) X(2, 3) \
     X(2, 4) X(2, 5) X(2, 6) X(2, 8) X(3, 1) X(3, 2) X(3, 3) X(3, 4) X(3, 5) X(4, 1) X(4, 2) X(4, 3) X(4, 4)
 
 // LDS bytes of one wave's step: 8 M A images, then their scale bytes.
@@ -328,13 +328,13 @@ struct F4Shape {
 };
 
 // Instantiated (steps per wave, quads) pairs, minus the two that spill
-// registers at this M.
+// registers at this M, and 9 quads (one step per wave) where M > 1.
 bool f4_instantiated(int64_t M, int spw, int q) {
     bool in = false;
 #define TERN_F4_CASE(SP, QQ) in = in || (spw == SP && q == QQ);
     TERN_F4_TABLE(TERN_F4_CASE)
 #undef TERN_F4_CASE
-    return in && !(M == 1 && spw == 1 && q == 17) && !(M == 4 && spw == 2 && q == 8);
+    return in && !(M == 1 && spw == 1 && q == 17) && !(M == 4 && spw == 2 && q == 8) && !(M > 1 && q == 9);
 }
 
 size_t f4_lds(int64_t M, int nw, int q) {
@@ -351,7 +351,10 @@ F4Shape f4_shape(int64_t M, int64_t N, int64_t K) {
     // (staging, reduction): pick the Q with the least of that, the larger Q
     // on ties.  Measured at M = 1 (rows 5120 / 17408): the best Q of a sweep
     // over 2..16 was also the model's choice, 5 / 6 (4.16 / 7.35 us); at
-    // 17408 -> 5120, 5 (7.04 us against 9.7 for 2).
+    // 17408 -> 5120, 5 (7.04 us against 9.7 for 2).  Nine quads, added
+    // later, put 5120 -> 17408 in two rounds of workgroups instead of three:
+    // 6.88 -> 6.78 us at M = 1 (in-process A/B); at M = 3 it was 1% slower,
+    // so it serves M = 1 only.
     constexpr int64_t kCUs = 256;
     const int64_t quads = (N + 3) / 4;
     int64_t best = -1;

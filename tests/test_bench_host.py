@@ -1,7 +1,7 @@
 """bench.py's host logic on the CPU: the counter-file readers, the kernel name
 parsing behind the traffic record, the traffic guard that drops a counter
-figure once the profiled kernel's machine code or the dispatch source
-changes, and the refusal to run on more than one GPU.  Nothing here touches
+figure once the profiled kernel's machine code or the library sources that
+pick the kernel change, and the refusal to run on more than one GPU.  Nothing here touches
 a GPU."""
 import json
 import os
@@ -75,7 +75,7 @@ def test_traffic_guard_drops_a_record_whose_code_hash_differs(tmp_path, monkeypa
     assert bench.measured_traffic("absent")[0] is None
 
 
-def test_traffic_guard_drops_a_record_of_another_dispatch_source(tmp_path, monkeypatch):
+def test_traffic_guard_drops_a_record_of_other_library_sources(tmp_path, monkeypatch):
     tern = pytest.importorskip("ternary_weight_matmul_amd", reason="libtern.so not built")
     funcs = bench.device_functions(tern.library_path())
     sym = sorted(s for s in funcs if "gemv_fp4_kernel" in s)[0]
@@ -85,7 +85,7 @@ def test_traffic_guard_drops_a_record_of_another_dispatch_source(tmp_path, monke
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))
     value, why = bench.measured_traffic("w")
-    assert value is None and "dispatch" in why
+    assert value is None and "library sources" in why
     rec["w"]["dispatch_sha256"] = bench.dispatch_sha256()
     path.write_text(json.dumps(rec))
     assert bench.measured_traffic("w") == (7, "p.md")
@@ -96,3 +96,16 @@ def test_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_library_source_hash_covers_the_kernel_files(tmp_path, monkeypatch):
+    """A change in a kernel file (where the launch shape of a shape is chosen),
+    not only in the ABI dispatch, changes the source hash."""
+    import shutil
+    shutil.copytree(os.path.join(ROOT, bench.DISPATCH_SOURCES), tmp_path / "csrc")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "DISPATCH_SOURCES", "csrc")
+    before = bench.dispatch_sha256()
+    with open(tmp_path / "csrc" / "tern_gemv_fp4.hip", "a") as f:
+        f.write("\n")
+    assert bench.dispatch_sha256() != before
