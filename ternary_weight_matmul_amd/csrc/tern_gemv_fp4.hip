@@ -328,13 +328,17 @@ struct F4Shape {
 };
 
 // Instantiated (steps per wave, quads) pairs, minus the two that spill
-// registers at this M, and 9 quads (one step per wave) where M > 1.
+// registers at this M, 9 quads (one step per wave) where M > 1, and 12 quads
+// (one step per wave) at M = 1: measured slower than 9 or 8 quads on every
+// width tried (M = 1, K = 5120: 8.76 / 8.64 / 13.2 us at 17408 / 15360 /
+// 34816 rows, against 6.71 / 6.21 / 11.0), though the tile model prefers it
+// at 34816.
 bool f4_instantiated(int64_t M, int spw, int q) {
     bool in = false;
 #define TERN_F4_CASE(SP, QQ) in = in || (spw == SP && q == QQ);
     TERN_F4_TABLE(TERN_F4_CASE)
 #undef TERN_F4_CASE
-    return in && !(M == 1 && spw == 1 && q == 17) && !(M == 4 && spw == 2 && q == 8) && !(M > 1 && q == 9);
+    return in && !(M == 1 && spw == 1 && (q == 17 || q == 12)) && !(M == 4 && spw == 2 && q == 8) && !(M > 1 && q == 9);
 }
 
 size_t f4_lds(int64_t M, int nw, int q) {
